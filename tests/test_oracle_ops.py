@@ -1,0 +1,424 @@
+"""Pins for the oracle's five epilogues (CPU only).
+
+Each function is checked against something other than itself: torch's CPU
+layer_norm / rms_norm / bf16 add / fp8 conversion, exact rational arithmetic
+(fractions, decimal), closed forms on constructed inputs, invariants, and the
+tie case the sglang PR 37116 page gives for bias_mul_add.
+"""
+import json
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import synth
+from exact import (bf16_ulp_distance, bf16_value, is_bf16_midpoint, nearest_bf16_bits,
+                   nearest_f32)
+
+RNG = np.random.default_rng(7)
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def bfbits(v) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf2f(bits) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def torch_e4m3(v32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(v32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def rn32_inv(s: float) -> np.float32:
+    return np.float32(1.0) / np.float32(s)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm + modulation + FP8
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 16, 32, 96])
+def test_layernorm_stats_are_correctly_rounded(oracle_mod, n):
+    getcontext().prec = 80
+    eps = np.float32(1e-6)
+    for _ in range(10):
+        v = bfbits(RNG.standard_normal(n) * 3.0 + RNG.standard_normal())
+        xs = [bf16_value(b) for b in v]
+        mean = sum(xs, Fraction(0)) / n
+        var = sum(((x - mean) ** 2 for x in xs), Fraction(0)) / n
+        t = var + Fraction(float(eps))
+        inv = Decimal(1) / (Decimal(t.numerator) / Decimal(t.denominator)).sqrt()
+        m, f = oracle_mod.layernorm_stats(v, float(eps))
+        assert m == nearest_f32(mean)
+        assert f == nearest_f32(Fraction(inv))
+
+
+def test_norm_matches_torch_layer_norm(oracle_mod):
+    # Rows at three magnitudes: eps matters for the smallest, not for the others.
+    H = 3072
+    x = np.concatenate([RNG.standard_normal((8, H)) * s for s in (1.0, 1e-3, 30.0)])
+    xb = bfbits(x).reshape(x.shape)
+    zeros = np.zeros(H, np.uint16)
+    eps = float(np.float32(1e-6))
+    y, _, _ = oracle_mod.norm_modulate_fp8(xb, zeros, zeros, 1.0, eps)
+    ref = F.layer_norm(torch.from_numpy(bf2f(xb).astype(np.float64)), (H,), eps=eps)
+    want = bfbits(ref.numpy().astype(np.float32))
+    dist = bf16_ulp_distance(y, want)
+    assert dist.max() <= 1
+    assert (dist == 0).mean() >= 0.999
+
+
+def test_norm_rows_have_zero_mean_unit_variance(oracle_mod):
+    H = 3072
+    for sigma in (0.5, 1.0, 4.0):
+        x = bfbits(RNG.standard_normal((4, H)) * sigma + 0.3).reshape(4, H)
+        zeros = np.zeros(H, np.uint16)
+        y, _, _ = oracle_mod.norm_modulate_fp8(x, zeros, zeros, 1.0, 1e-6)
+        yf = bf2f(y).astype(np.float64)
+        xf = bf2f(x).astype(np.float64)
+        var_x = xf.var(axis=1)
+        assert np.all(np.abs(yf.mean(axis=1)) <= 2.0**-8)
+        expect = var_x / (var_x + 1e-6)
+        assert np.all(np.abs(yf.var(axis=1) - expect) <= 2.0**-7)
+
+
+def test_norm_modulate_closed_form_alternating_rows(oracle_mod):
+    # Rows +-1 alternating: mean 0, variance 1, so the normalised row is exactly
+    # +-1 after bf16 rounding and y = sign * (1 + scale) + shift exactly.
+    H = 512
+    sign = np.where(np.arange(H) % 2 == 0, 1.0, -1.0)
+    x = bfbits(np.stack([sign, -sign]))
+    s_choices = np.array([-0.5, -0.25, 0.0, 0.125, 0.25, 0.5, 0.75])
+    h_choices = np.array([-1.0, -0.375, 0.0, 0.25, 0.625])
+    scale = RNG.choice(s_choices, H)
+    shift = RNG.choice(h_choices, H)
+    y, q, _ = oracle_mod.norm_modulate_fp8(x, bfbits(scale), bfbits(shift), 0.0625, 1e-6)
+    want = np.stack([sign * (1 + scale) + shift, -sign * (1 + scale) + shift])
+    assert np.array_equal(bf2f(y), want.astype(np.float32))
+    assert np.array_equal(q, torch_e4m3(np.clip(want * 16.0, -448, 448)))
+
+
+def test_constant_row_gives_shift(oracle_mod):
+    H = 256
+    x = bfbits(np.full((3, H), 2.5))
+    scale = bfbits(RNG.standard_normal(H) * 0.1)
+    shift = bfbits(RNG.standard_normal(H))
+    y, q, _ = oracle_mod.norm_modulate_fp8(x, scale, shift, 0.02, 1e-6)
+    assert np.array_equal(y, np.broadcast_to(shift, (3, H)))
+    inv = rn32_inv(0.02)
+    want_q = torch_e4m3(np.clip(bf2f(shift) * inv, -448, 448))
+    assert np.array_equal(q, np.broadcast_to(want_q, (3, H)))
+
+
+@pytest.mark.parametrize("input_scale", [0.02, 0.0625, 0.5, 0.4754464328])
+def test_fp8_split_equals_fused(oracle_mod, input_scale):
+    inp = synth.norm_modulate_inputs(rows=32, hidden=3072, seed=11, input_scale=input_scale)
+    y, q, pre = oracle_mod.norm_modulate_fp8(
+        synth.bf16_bits(inp.x), synth.bf16_bits(inp.scale), synth.bf16_bits(inp.shift),
+        inp.input_scale, inp.eps)
+    inv = rn32_inv(inp.input_scale)
+    split = torch.from_numpy(bf2f(y)).mul(float(inv)).clamp(-448, 448)
+    assert np.array_equal(q, split.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert np.array_equal(pre, split.numpy())
+    assert not np.any((q & 0x7F) == 0x7F)
+
+
+# ---------------------------------------------------------------------------
+# Gated residual (+ optional bias)
+# ---------------------------------------------------------------------------
+
+def _tie_products(n_want: int):
+    """(xb, gate) bf16 pairs whose exact product is a bf16 midpoint."""
+    out = []
+    while len(out) < n_want:
+        a = bfbits(RNG.standard_normal(4096) * 4)
+        g = bfbits(RNG.standard_normal(4096) * 4)
+        for x, y in zip(a, g):
+            if is_bf16_midpoint(bf16_value(x) * bf16_value(y)):
+                out.append((x, y))
+    return out[:n_want]
+
+
+def test_gated_residual_is_one_exact_rounding(oracle_mod):
+    H = 64
+    rows = 6
+    x = bfbits(RNG.standard_normal((rows, H))).reshape(rows, H)
+    res = bfbits(RNG.standard_normal((rows, H))).reshape(rows, H)
+    bias = bfbits(RNG.standard_normal(H) * 0.02)
+    gate = bfbits(RNG.standard_normal(H) * 0.1 + 1)
+    ties = _tie_products(H)
+    # Row 0: the exact product lands on a bf16 midpoint; residual nudges it.
+    nudges = bfbits(RNG.choice([1e-3, -1e-3, 0.0], H))
+    x[0] = [t[0] for t in ties]
+    gate_t = np.array([t[1] for t in ties], np.uint16)
+    res[0] = nudges
+    zeros = np.zeros(H, np.uint16)
+    for g_row, bias_arg in ((gate, bias), (gate_t, None)):
+        r_out, _, _, _ = oracle_mod.scale_residual_norm_modulate_fp8(
+            x, bias_arg, g_row, res, zeros, zeros, 1.0, 1e-6)
+        for i in range(rows):
+            xb = bf2f(x[i])
+            if bias_arg is not None:
+                xb = bf2f(bfbits(xb + bf2f(bias_arg)))  # numpy fp32 add, torch bf16 RNE
+            for j in range(H):
+                exact = Fraction(float(bf2f(res[i, j]))) + Fraction(float(bf2f(g_row[j]))) * Fraction(float(xb[j]))
+                assert r_out[i, j] == nearest_bf16_bits(exact), (i, j)
+
+
+def test_scale_residual_equals_norm_of_residual_out(oracle_mod):
+    inp = synth.scale_residual_inputs(rows=24, hidden=3072, seed=5, input_scale=0.02)
+    b = synth.bf16_bits
+    r, y, q, pre = oracle_mod.scale_residual_norm_modulate_fp8(
+        b(inp.x), b(inp.bias), b(inp.gate), b(inp.residual), b(inp.scale), b(inp.shift),
+        inp.input_scale, inp.eps)
+    y2, q2, pre2 = oracle_mod.norm_modulate_fp8(r, b(inp.scale), b(inp.shift), inp.input_scale,
+                                                 inp.eps)
+    assert np.array_equal(y, y2) and np.array_equal(q, q2) and np.array_equal(pre, pre2)
+    # gate = 0: residual passes through untouched.
+    zero_gate = np.zeros_like(b(inp.gate))
+    r0, _, _, _ = oracle_mod.scale_residual_norm_modulate_fp8(
+        b(inp.x), b(inp.bias), zero_gate, b(inp.residual), b(inp.scale), b(inp.shift),
+        inp.input_scale, inp.eps)
+    assert np.array_equal(r0, b(inp.residual))
+
+
+# ---------------------------------------------------------------------------
+# bias_mul_add
+# ---------------------------------------------------------------------------
+
+def test_bias_mul_add_golden_tie_case(oracle_mod):
+    with open(os.path.join(GOLDEN, "bias_mul_add_tie.json")) as f:
+        case = json.load(f)["inputs"]
+    x, bias, gate, res = (bfbits([case[k]]) for k in ("x", "bias", "gate", "residual"))
+    for k, v in zip(("x", "bias", "gate", "residual"), (x, bias, gate, res)):
+        assert bf2f(v)[0] == np.float32(case[k]), k  # the page's inputs are bf16 values
+    y = oracle_mod.bias_mul_add(x.reshape(1, 1), bias, gate, res.reshape(1, 1))
+    biased = bf16_value(bfbits(bf2f(x) + bf2f(bias))[0])
+    exact = biased * bf16_value(gate[0]) + bf16_value(res[0])
+    want = nearest_bf16_bits(exact)
+    assert y[0, 0] == want
+    # The product alone is a bf16 midpoint: a two-step fp32 path rounds differently.
+    two_step = bfbits(np.float32(biased * bf16_value(gate[0])) + bf2f(res))[0]
+    assert two_step != want
+
+
+def test_bias_mul_add_special_cases(oracle_mod):
+    inp = synth.bias_mul_add_inputs(rows=16, hidden=512, seed=2)
+    b = synth.bf16_bits
+    y0 = oracle_mod.bias_mul_add(b(inp.x), b(inp.bias), np.zeros(512, np.uint16), b(inp.residual))
+    assert np.array_equal(y0, b(inp.residual))
+    one = bfbits(np.ones(512))
+    y1 = oracle_mod.bias_mul_add(b(inp.x), None, one, b(inp.residual))
+    assert np.array_equal(y1, b(inp.x + inp.residual))  # torch CPU bf16 add
+
+
+def test_bias_mul_add_matches_exact_rationals(oracle_mod):
+    rows, H = 4, 96
+    inp = synth.bias_mul_add_inputs(rows=rows, hidden=H, seed=9)
+    b = synth.bf16_bits
+    x, bias, gate, res = b(inp.x), b(inp.bias), b(inp.gate), b(inp.residual)
+    ties = _tie_products(H)  # (biased, gate) pairs on a midpoint; x chosen so bias keeps it
+    x[0] = [t[0] for t in ties]
+    bias = np.zeros(H, np.uint16)
+    gate = np.array([t[1] for t in ties], np.uint16)
+    res[0] = bfbits(RNG.choice([2.0**-20, -(2.0**-20), 0.0], H))
+    y = oracle_mod.bias_mul_add(x, bias, gate, res)
+    for i in range(rows):
+        biased = bf2f(bfbits(bf2f(x[i]) + bf2f(bias)))
+        for j in range(H):
+            exact = Fraction(float(biased[j])) * bf16_value(gate[j]) + bf16_value(res[i, j])
+            assert y[i, j] == nearest_bf16_bits(exact), (i, j)
+
+
+# ---------------------------------------------------------------------------
+# QKV epilogue
+# ---------------------------------------------------------------------------
+
+def _qkv_small(seed=0, img_rows=5, txt_rows=3, heads=3, img_eps=1e-6, txt_eps=0.25):
+    return synth.qkv_inputs(img_rows=img_rows, txt_rows=txt_rows, heads=heads, head_dim=128,
+                            seed=seed, img_eps=img_eps, txt_eps=txt_eps)
+
+
+def _run_oracle_qkv(oracle_mod, inp, cos=None, sin=None):
+    b = synth.bf16_bits
+    ic, is_, tc, ts = inp.img_cos, inp.img_sin, inp.txt_cos, inp.txt_sin
+    if cos is not None:
+        ic, tc = np.full_like(ic, cos), np.full_like(tc, cos)
+        is_, ts = np.full_like(is_, sin), np.full_like(ts, sin)
+    return oracle_mod.qkv_epilogue_packed(
+        b(inp.img_qkv), b(inp.txt_qkv), b(inp.img_q_w), b(inp.img_k_w), b(inp.txt_q_w),
+        b(inp.txt_k_w), ic, is_, tc, ts, inp.heads, inp.head_dim, inp.img_eps, inp.txt_eps)
+
+
+def test_qk_rmsnorm_matches_torch_rms_norm(oracle_mod):
+    inp = _qkv_small()
+    jq, jk, _ = _run_oracle_qkv(oracle_mod, inp, cos=1.0, sin=0.0)  # identity rotation
+    D, Hh = inp.head_dim, inp.heads
+    for part, out, (iw, tw) in ((0, jq, (inp.img_q_w, inp.txt_q_w)),
+                                (1, jk, (inp.img_k_w, inp.txt_k_w))):
+        for stream, w, eps, rows in (("txt", tw, inp.txt_eps, slice(0, 3)),
+                                     ("img", iw, inp.img_eps, slice(3, 8))):
+            t = (inp.txt_qkv if stream == "txt" else inp.img_qkv)
+            x = t[:, part * Hh * D:(part + 1) * Hh * D].reshape(-1, Hh, D).double()
+            ref = F.rms_norm(x, (D,), weight=w.double(), eps=float(np.float32(eps)))
+            want = bfbits(ref.numpy().astype(np.float32)).reshape(-1, Hh, D)
+            dist = bf16_ulp_distance(out[rows], want)
+            assert dist.max() <= 1
+            assert (dist == 0).mean() >= 0.998
+
+
+def test_rope_is_complex_rotation_rounded_once(oracle_mod):
+    inp = _qkv_small(seed=4)
+    nq, nk, _ = _run_oracle_qkv(oracle_mod, inp, cos=1.0, sin=0.0)
+    oq, ok, _ = _run_oracle_qkv(oracle_mod, inp)
+    cos = np.concatenate([inp.txt_cos, inp.img_cos])  # joint order: text first
+    sin = np.concatenate([inp.txt_sin, inp.img_sin])
+    for n, o in ((nq, oq), (nk, ok)):
+        nf = bf2f(n).astype(np.float64)
+        z = (nf[..., 0::2] + 1j * nf[..., 1::2]) * (cos + 1j * sin)[:, None, :]
+        want = np.empty_like(n)
+        want[..., 0::2] = bfbits(z.real.astype(np.float32))
+        want[..., 1::2] = bfbits(z.imag.astype(np.float32))
+        dist = bf16_ulp_distance(o, want)
+        assert dist.max() <= 1 and (dist == 0).mean() >= 0.998
+        # Exactly: one rounding of the exact rotated value.
+        for j in range(0, o.shape[0], 3):
+            for h in range(o.shape[1]):
+                for p in range(0, 64, 7):
+                    n0 = Fraction(float(nf[j, h, 2 * p]))
+                    n1 = Fraction(float(nf[j, h, 2 * p + 1]))
+                    c = Fraction(float(cos[j, p]))
+                    s = Fraction(float(sin[j, p]))
+                    assert o[j, h, 2 * p] == nearest_bf16_bits(n0 * c - n1 * s)
+                    assert o[j, h, 2 * p + 1] == nearest_bf16_bits(n1 * c + n0 * s)
+        # The rotation preserves each pair's length (to bf16 rounding).
+        of = bf2f(o).astype(np.float64)
+        ln = np.hypot(nf[..., 0::2], nf[..., 1::2])
+        lo = np.hypot(of[..., 0::2], of[..., 1::2])
+        assert np.all(np.abs(lo - ln) <= 2.0**-7 * ln + 1e-30)
+
+
+def test_qkv_layout_v_copy_and_joint_order(oracle_mod):
+    inp = _qkv_small(seed=8)
+    jq, jk, jv = _run_oracle_qkv(oracle_mod, inp)
+    b = synth.bf16_bits
+    w = inp.width
+    tv = b(inp.txt_qkv)[:, 2 * w:].reshape(-1, inp.heads, inp.head_dim)
+    iv = b(inp.img_qkv)[:, 2 * w:].reshape(-1, inp.heads, inp.head_dim)
+    assert np.array_equal(jv[:3], tv) and np.array_equal(jv[3:], iv)
+    # Contiguous inputs give the same result as the packed, strided views.
+    tq, tk, tvv = (np.ascontiguousarray(b(x)) for x in inp.views("txt"))
+    iq, ik, ivv = (np.ascontiguousarray(b(x)) for x in inp.views("img"))
+    out = oracle_mod.qkv_epilogue(
+        iq.ctypes.data, ik.ctypes.data, ivv.ctypes.data, w, tq.ctypes.data, tk.ctypes.data,
+        tvv.ctypes.data, w, 5, 3, b(inp.img_q_w), b(inp.img_k_w), b(inp.txt_q_w),
+        b(inp.txt_k_w), inp.img_cos, inp.img_sin, inp.txt_cos, inp.txt_sin, inp.heads,
+        inp.head_dim, inp.img_eps, inp.txt_eps)
+    for a, c in zip(out, (jq, jk, jv)):
+        assert np.array_equal(a, c)
+
+
+def test_qk_rmsnorm_unit_weight_gives_unit_rms(oracle_mod):
+    inp = _qkv_small(seed=3, txt_eps=1e-6)
+    one = torch.ones(128, dtype=torch.bfloat16)
+    inp.img_q_w = inp.img_k_w = inp.txt_q_w = inp.txt_k_w = one
+    jq, jk, _ = _run_oracle_qkv(oracle_mod, inp, cos=1.0, sin=0.0)
+    for o in (jq, jk):
+        rms = np.sqrt((bf2f(o).astype(np.float64) ** 2).mean(axis=-1))
+        assert np.all(np.abs(rms - 1.0) <= 2.0**-8)
+
+
+# ---------------------------------------------------------------------------
+# Token concatenation + FP8 / FP4
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("input_scale", [0.05, 0.5, 0.4754464328])
+def test_token_cat_fp8_equals_torch_cat_then_quantise(oracle_mod, input_scale):
+    inp = synth.token_cat_inputs(rows=7, a_cols=96, b_cols=160, seed=1, fp8_scale=input_scale)
+    b = synth.bf16_bits
+    q, _ = oracle_mod.token_cat_fp8(b(inp.attn), b(inp.mlp), inp.fp8_scale)
+    cat = torch.cat([inp.attn, inp.mlp], dim=1).float()
+    ref = (cat * float(rn32_inv(inp.fp8_scale))).clamp(-448, 448).to(torch.float8_e4m3fn)
+    assert np.array_equal(q, ref.view(torch.uint8).numpy())
+    qa, _ = oracle_mod.token_cat_fp8(b(inp.attn), np.zeros((7, 0), np.uint16), inp.fp8_scale)
+    qb, _ = oracle_mod.token_cat_fp8(b(inp.mlp), np.zeros((7, 0), np.uint16), inp.fp8_scale)
+    assert np.array_equal(q, np.concatenate([qa, qb], axis=1))
+
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+@pytest.mark.parametrize("k,j", [(0, 0), (-3, 3), (2, -2), (-5, 6)])
+def test_fp4_closed_form_grid_groups(oracle_mod, k, j):
+    rows, a_cols, b_cols = 3, 32, 16
+    cols = a_cols + b_cols
+    idx = RNG.integers(0, 8, (rows, cols))
+    neg = RNG.integers(0, 2, (rows, cols)).astype(bool)
+    idx[:, ::16] = 7  # every group holds a +-6 * 2^k, so amax = 6 * 2^k
+    vals = np.where(neg, -1.0, 1.0) * _E2M1[idx] * 2.0**k
+    x = bfbits(vals).reshape(rows, cols)
+    assert np.array_equal(bf2f(x), vals.astype(np.float32))
+    g = 2.0**j
+    packed, scales, s_pre, _ = oracle_mod.token_cat_fp4(x[:, :a_cols], x[:, a_cols:], g)
+    # s_pre = (6 * 2^k / 6) * 2^j is exactly an E4M3 value; x * k_scale hits the grid.
+    assert np.all(s_pre == np.float32(2.0 ** (k + j)))
+    want_scale = torch_e4m3(np.float32([2.0 ** (k + j)]))[0]
+    assert np.all(scales[:rows] == want_scale) and np.all(scales[rows:] == 0)
+    codes = (idx | np.where(neg & (idx > 0), 8, 0)) | np.where(neg & (idx == 0), 8, 0)
+    want_packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(packed, want_packed)
+
+
+def test_fp4_zero_group_saturation_and_padding(oracle_mod):
+    rows, cols = 17, 64
+    v = RNG.standard_normal((rows, cols))
+    v[:, 16:32] = 0.0  # one all-zero group per row
+    x = bfbits(v).reshape(rows, cols)
+    packed, scales, _, _ = oracle_mod.token_cat_fp4(x[:, :32], x[:, 32:], 448.0 * 6 / 4.0)
+    assert scales.shape == (128, 4)
+    assert np.all(scales[:, 1] == 0) and np.all(packed[:, 8:16] == 0)
+    assert np.all(scales[rows:] == 0)
+    # Saturating global scale: every nonzero group's scale is 448, its largest element +-6.
+    packed, scales, _, _ = oracle_mod.token_cat_fp4(x[:, :32], x[:, 32:], 1e4)
+    big = np.abs(bf2f(x)).reshape(rows, 4, 16).max(axis=2) > 0.3
+    assert np.all(scales[:rows][big] == 0x7E)
+    nib = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(rows, cols)
+    amax_pos = np.abs(bf2f(x)).reshape(rows, 4, 16).argmax(axis=2)
+    for r in range(rows):
+        for gi in range(4):
+            if big[r, gi]:
+                assert nib[r, gi * 16 + amax_pos[r, gi]] & 7 == 7
+
+
+def test_fp4_dequantisation_error_bound_and_branch_split(oracle_mod):
+    inp = synth.token_cat_inputs(rows=9, a_cols=64, b_cols=192, seed=6)
+    b = synth.bf16_bits
+    a_bits, m_bits = b(inp.attn), b(inp.mlp)
+    packed, scales, s_pre, pre = oracle_mod.token_cat_fp4(a_bits, m_bits, inp.fp4_g)
+    x = bf2f(np.concatenate([a_bits, m_bits], axis=1)).astype(np.float64)
+    codes = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(x.shape)
+    dec_s = oracle_mod.e4m3_decode(scales[:9]).repeat(16, axis=1)
+    deq = oracle_mod.e2m1_decode(codes) * dec_s / inp.fp4_g
+    kx = np.abs(x) * inp.fp4_g / dec_s
+    half_gap = np.where(kx < 2, 0.25, np.where(kx < 4, 0.5, 1.0))
+    ok = kx <= 6.0
+    bound = half_gap * dec_s / inp.fp4_g * (1 + 2.0**-20)
+    assert np.all(np.abs(x - deq)[ok] <= bound[ok])
+    # An element can exceed 6 only when its group's E4M3 scale rounded down, which
+    # is by at most 2^-4 relative, so it must lie within 2^-4 of the group maximum.
+    amax = np.abs(x).reshape(9, -1, 16).max(axis=2).repeat(16, axis=1)
+    assert np.all(np.abs(x)[~ok] >= amax[~ok] * (1 - 2.0**-4) * (1 - 2.0**-20))
+    assert (~ok).mean() < 0.05
+    # Groups never straddle the branch boundary: quantising each branch alone agrees.
+    pa, sa, _, _ = oracle_mod.token_cat_fp4(a_bits, np.zeros((9, 0), np.uint16), inp.fp4_g)
+    pb, sb, _, _ = oracle_mod.token_cat_fp4(m_bits, np.zeros((9, 0), np.uint16), inp.fp4_g)
+    assert np.array_equal(packed, np.concatenate([pa, pb], axis=1))
+    assert np.array_equal(scales, np.concatenate([sa, sb], axis=1))
