@@ -1,0 +1,216 @@
+/*
+ * dit_epilogues.h -- C ABI of the fused, memory-bound, row-wise epilogues of a
+ * diffusion-transformer block, implemented as HIP kernels for gfx950 (MI355X).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer. BF16 tensors are passed as
+ *    void* (raw 16-bit bfloat16 patterns); FP8 E4M3FN and packed FP4 outputs
+ *    as uint8_t*. Matrices are row-major; unless a stride argument says
+ *    otherwise, rows are dense.
+ *  - The caller owns and allocates every buffer. The library never allocates,
+ *    frees or synchronises; each call enqueues its work on `stream` (a
+ *    hipStream_t passed as void*; NULL is the default stream) and returns.
+ *    Calls contain no host<->device copies and no host reads of device data,
+ *    so they can be captured into a HIP graph.
+ *  - Static quantisation scales (`input_scale_dev`, `scale_dev`) are device
+ *    pointers to ONE fp32 value, read by the kernel only. Preconditions that
+ *    are documented but NOT checked: scales are finite and > 0, inputs are
+ *    finite, and no output overlaps any input or another output.
+ *  - Return value: DIT_OK (0) or a dit_status code. On any refusal the call
+ *    enqueues nothing and outputs are untouched, so a caller can fall back to
+ *    an unfused path. The reason is also available from dit_last_error()
+ *    (per thread). rows == 0 is a successful no-op.
+ *  - Validation is host-only and happens before any HIP call: NULL pointers
+ *    (DIT_ERR_NULL), negative or inconsistent sizes (DIT_ERR_SHAPE), pointers
+ *    not 16-byte aligned (DIT_ERR_ALIGN), shapes outside the instantiated
+ *    kernels (DIT_ERR_UNSUPPORTED). A failing launch returns DIT_ERR_HIP.
+ *
+ * Sources: the five sglang pull-request summary pages on prhub.com.cn that
+ * describe these fusions (PRs 37123, 37156, 37162, 37116, 37141). Each entry
+ * point names the page and section that define what it computes.
+ */
+#ifndef DIT_EPILOGUES_H
+#define DIT_EPILOGUES_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_ABI_VERSION 1
+
+typedef enum dit_status {
+    DIT_OK = 0,
+    DIT_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    DIT_ERR_SHAPE = 2,       /* negative / inconsistent sizes or strides      */
+    DIT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned              */
+    DIT_ERR_UNSUPPORTED = 4, /* valid arguments no kernel is built for        */
+    DIT_ERR_HIP = 5          /* the HIP runtime refused the launch            */
+} dit_status;
+
+/* ABI version of the loaded library (DIT_ABI_VERSION at build time). */
+int dit_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* dit_status_string(int status);
+
+/* Message describing the most recent refusal on the calling thread ("" if the
+ * last call succeeded). The pointer stays valid until the thread's next call. */
+const char* dit_last_error(void);
+
+/*
+ * LayerNorm without affine + AdaLN modulation + static FP8 E4M3 quantisation,
+ * dual output.
+ *
+ * Defined by: sglang PR 37156 page ("Implementation breakdown" items 1-2 and
+ * the norm_scale_shift excerpt under "Key source snippets"): one row per block;
+ * LayerNorm without weight or bias with fp32 statistics; the normalised value
+ * is rounded to bf16; y = bf16(norm * (1 + scale) + shift); the FP8 output is
+ * e4m3(clamp(y * (1 / input_scale), -448, 448)). Both outputs are written.
+ *
+ *   y      [rows, hidden] bf16, out
+ *   q      [rows, hidden] E4M3FN bytes, out
+ *   x      [rows, hidden] bf16, in
+ *   scale, shift  [hidden] bf16, in (broadcast over rows)
+ *   input_scale_dev  device fp32 scalar (static FP8 scale; q = y / scale)
+ *   eps    LayerNorm epsilon (host fp32)
+ *
+ * Statistics: mean and biased variance per row; 1 / input_scale is IEEE fp32
+ * division. hidden must be a multiple of 8 and at most 6144 (the row is held
+ * in registers), else DIT_ERR_UNSUPPORTED.
+ */
+int dit_norm_modulate_fp8(void* y, uint8_t* q, const void* x, const void* scale,
+                          const void* shift, const float* input_scale_dev,
+                          int64_t rows, int64_t hidden, float eps, void* stream);
+
+/*
+ * Optional input bias + gated residual, then the same LayerNorm + modulation +
+ * FP8 as dit_norm_modulate_fp8, writing the new residual too.
+ *
+ * Defined by: sglang PR 37156 page ("Implementation breakdown" item 2: the
+ * residual variant returns normalised + quantised + residual_out) and sglang
+ * PR 37116 page ("Implementation breakdown" item 3: x + bias folded into the
+ * gated-residual LayerNorm kernel; the fallback forms a bf16 x + bias first).
+ *
+ *   residual_out [rows, hidden] bf16, out:
+ *       bf16(residual + gate * xb) with ONE rounding, xb = bf16(x + bias)
+ *       (xb = x when bias is NULL)
+ *   y, q         as dit_norm_modulate_fp8, computed from residual_out
+ *   x, residual  [rows, hidden] bf16, in
+ *   bias         [hidden] bf16, in, NULLABLE
+ *   gate, scale, shift  [hidden] bf16, in
+ *   input_scale_dev, eps  as dit_norm_modulate_fp8
+ *
+ * Same shape limits as dit_norm_modulate_fp8.
+ */
+int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q,
+                                         const void* x, const void* bias,
+                                         const void* gate, const void* residual,
+                                         const void* scale, const void* shift,
+                                         const float* input_scale_dev,
+                                         int64_t rows, int64_t hidden, float eps,
+                                         void* stream);
+
+/*
+ * QKV epilogue: per-head RMSNorm of Q and K, interleaved RoPE, V copy, and the
+ * joint [text, image] packing, reading Q/K/V straight from the packed QKV GEMM
+ * output through strided views.
+ *
+ * Defined by: sglang PR 37123 page ("Implementation breakdown" items 3-4 and
+ * the forward excerpt under "Key source snippets"): Q and K get an RMS
+ * normalisation per head with their stream's weight and epsilon, then
+ * interleaved (non-NeoX) RoPE from an fp32 cache; V is copied; outputs are
+ * written in [text, image] order.
+ *
+ *   joint_q, joint_k, joint_v  [txt_rows + img_rows, heads, head_dim] bf16, out;
+ *       joint row j < txt_rows is text row j, row txt_rows + i is image row i
+ *   img_q, img_k, img_v  bf16 in; row i, head h starts at element
+ *       i * img_row_stride + h * head_dim (e.g. column views of a packed
+ *       [img_rows, 3 * heads * head_dim] buffer, stride 3 * heads * head_dim)
+ *   txt_q, txt_k, txt_v  the same for the text stream
+ *   *_row_stride  in ELEMENTS; >= heads * head_dim and a multiple of 8
+ *   img_q_w, img_k_w, txt_q_w, txt_k_w  [head_dim] bf16 RMSNorm weights
+ *   img_cos, img_sin  [img_rows, head_dim / 2] fp32; txt_cos, txt_sin
+ *       [txt_rows, head_dim / 2] fp32. Pair (2i, 2i+1) of a row rotates by the
+ *       angle whose cos/sin are entry i of that row:
+ *       (a, b) -> (a cos - b sin, b cos + a sin)
+ *   img_eps, txt_eps  RMSNorm epsilons
+ *
+ * head_dim must be 128 (else DIT_ERR_UNSUPPORTED); heads in [1, 64].
+ * Either stream may have zero rows.
+ */
+int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v,
+                     const void* img_q, const void* img_k, const void* img_v,
+                     int64_t img_rows, int64_t img_row_stride,
+                     const void* txt_q, const void* txt_k, const void* txt_v,
+                     int64_t txt_rows, int64_t txt_row_stride,
+                     const void* img_q_w, const void* img_k_w,
+                     const void* txt_q_w, const void* txt_k_w,
+                     const float* img_cos, const float* img_sin,
+                     const float* txt_cos, const float* txt_sin,
+                     int32_t heads, int32_t head_dim, float img_eps, float txt_eps,
+                     void* stream);
+
+/*
+ * Final gated residual with an absorbed output bias: y = (x + bias) * gate +
+ * residual.
+ *
+ * Defined by: sglang PR 37116 page (the bias_mul_add excerpt under "Key source
+ * snippets" and the review highlights): the bias add is rounded to bf16, then
+ * the multiply-add is one native bf16 FMA, i.e. rounded ONCE.
+ *
+ *   y         [rows, hidden] bf16, out
+ *   x, residual  [rows, hidden] bf16, in
+ *   bias      [hidden] bf16, in, NULLABLE (no bias add)
+ *   gate      [hidden] bf16, in
+ *
+ * hidden must be a multiple of 8 (and at most 2^30).
+ */
+int dit_bias_mul_add(void* y, const void* x, const void* bias, const void* gate,
+                     const void* residual, int64_t rows, int64_t hidden,
+                     void* stream);
+
+/* Quantisation kinds of dit_token_cat_quant. */
+#define DIT_QUANT_FP8_E4M3 0
+#define DIT_QUANT_FP4_E2M1 1
+
+/*
+ * Token concatenation [a | b] fused with static FP8 or 16-element-group FP4
+ * quantisation; the concatenated bf16 row is never written.
+ *
+ * Defined by: sglang PR 37162 page (the _token_cat_fp8_kernel excerpt under
+ * "Key source snippets": a column left of the attention width reads the
+ * attention branch, else the MLP branch; values * (1 / scale), clamped to the
+ * E4M3 range) and sglang PR 37141 page ("Implementation breakdown" item 1: one
+ * 16-element group per GPU thread, packed E2M1 values with one E4M3 scale per
+ * group, zero scales for pad rows; the global scale argument is an inverse
+ * scale).
+ *
+ *   kind      DIT_QUANT_FP8_E4M3 or DIT_QUANT_FP4_E2M1
+ *   out       FP8: [rows, a_cols + b_cols] E4M3 bytes
+ *             FP4: [rows, (a_cols + b_cols) / 2] bytes, element 2k in the low
+ *             nibble of byte k, element 2k+1 in the high nibble
+ *   out_scales  FP4 only (ignored for FP8): [round_up(rows, 128),
+ *             (a_cols + b_cols) / 16] E4M3 bytes, row-major; the pad rows
+ *             [rows, round_up(rows, 128)) are written as 0x00
+ *   a         [rows, a_cols] bf16 (attention branch), in
+ *   b         [rows, b_cols] bf16 (MLP branch), in; may be NULL iff b_cols == 0
+ *   scale_dev device fp32 scalar. FP8: the static input scale s (codes are
+ *             e4m3(clamp(x * (1/s)))). FP4: the global INVERSE scale g; per
+ *             group s8 = e4m3(min((amax / 6) * g, 448)), codes
+ *             e2m1(x * (g / s8)), all codes 0 when s8 == 0.
+ *
+ * a_cols and b_cols must be multiples of 16 (a group never straddles the
+ * branch boundary) and a_cols >= 16.
+ */
+int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales,
+                        const void* a, int64_t a_cols, const void* b,
+                        int64_t b_cols, int64_t rows, const float* scale_dev,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIT_EPILOGUES_H */

@@ -1,0 +1,133 @@
+"""Fused DiT-block epilogues for MI355X (gfx950): HIP kernels behind a C ABI.
+
+The five entry points of include/dit_epilogues.h are exposed with the same
+names (``dit_*``, raw pointers and sizes, caller-allocated outputs), plus
+allocating conveniences that take and return torch device tensors:
+
+  norm_modulate_fp8                 -> (y bf16, q e4m3 bytes)
+  scale_residual_norm_modulate_fp8  -> (residual_out, y, q)
+  qkv_epilogue                      -> (joint_q, joint_k, joint_v)
+  bias_mul_add                      -> y
+  token_cat_quant                   -> FP8 bytes, or (FP4 packed bytes, scales)
+
+torch provides device memory and streams only; all arithmetic runs in the
+library's kernels, and nothing falls back to the CPU.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._native import (  # noqa: F401
+    DIT_ERR_ALIGN, DIT_ERR_HIP, DIT_ERR_NULL, DIT_ERR_SHAPE, DIT_ERR_UNSUPPORTED, DIT_OK,
+    DIT_QUANT_FP4_E2M1, DIT_QUANT_FP8_E4M3, LIB_PATH, DitError, dit_bias_mul_add,
+    dit_norm_modulate_fp8, dit_qkv_epilogue, dit_scale_residual_norm_modulate_fp8,
+    dit_token_cat_quant, header_symbols, last_error, lib, status_string,
+)
+
+
+def _dense_bf16(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+
+
+def _scalar_f32(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.float32 or t.numel() != 1 or not t.is_cuda:
+        raise ValueError(f"{name} must be a one-element fp32 device tensor")
+
+
+def norm_modulate_fp8(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                      input_scale: torch.Tensor, eps: float = 1e-6):
+    """LayerNorm (no affine) + AdaLN scale/shift + static FP8: returns (y, q)."""
+    for t, n in ((x, "x"), (scale, "scale"), (shift, "shift")):
+        _dense_bf16(t, n)
+    _scalar_f32(input_scale, "input_scale")
+    hidden = x.shape[-1]
+    y = torch.empty_like(x)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    dit_norm_modulate_fp8(y, q, x, scale, shift, input_scale, x.numel() // hidden, hidden, eps)
+    return y, q
+
+
+def scale_residual_norm_modulate_fp8(x, bias, gate, residual, scale, shift, input_scale,
+                                     eps: float = 1e-6):
+    """bias (optional) + gated residual, then norm/modulate/FP8:
+    returns (residual_out, y, q)."""
+    for t, n in ((x, "x"), (gate, "gate"), (residual, "residual"), (scale, "scale"),
+                 (shift, "shift")):
+        _dense_bf16(t, n)
+    if bias is not None:
+        _dense_bf16(bias, "bias")
+    _scalar_f32(input_scale, "input_scale")
+    hidden = x.shape[-1]
+    r = torch.empty_like(x)
+    y = torch.empty_like(x)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    dit_scale_residual_norm_modulate_fp8(r, y, q, x, bias, gate, residual, scale, shift,
+                                         input_scale, x.numel() // hidden, hidden, eps)
+    return r, y, q
+
+
+def _row_view(t: torch.Tensor, width: int, name: str) -> int:
+    """Row stride (elements) of a [rows, width] bf16 view with unit column stride."""
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or t.shape[1] != width or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a [rows, {width}] bf16 view with unit column stride")
+    return t.stride(0)
+
+
+def qkv_epilogue(img_q, img_k, img_v, txt_q, txt_k, txt_v, img_q_w, img_k_w, txt_q_w,
+                 txt_k_w, img_cos, img_sin, txt_cos, txt_sin, heads: int,
+                 img_eps: float = 1e-6, txt_eps: float = 1e-6, head_dim: int = 128):
+    """Q/K RMSNorm + interleaved RoPE + V copy into joint [text, image] buffers.
+    img_*/txt_* are [rows, heads * head_dim] views (e.g. column slices of the
+    packed QKV GEMM output). Returns (joint_q, joint_k, joint_v), each
+    [txt_rows + img_rows, heads, head_dim]."""
+    width = heads * head_dim
+    img_stride = _row_view(img_q, width, "img_q")
+    txt_stride = _row_view(txt_q, width, "txt_q")
+    for t, n, st in ((img_k, "img_k", img_stride), (img_v, "img_v", img_stride),
+                     (txt_k, "txt_k", txt_stride), (txt_v, "txt_v", txt_stride)):
+        if _row_view(t, width, n) != st:
+            raise ValueError(f"{n} must share its stream's row stride")
+    n_tok = img_q.shape[0] + txt_q.shape[0]
+    out = [torch.empty((n_tok, heads, head_dim), dtype=torch.bfloat16, device=img_q.device)
+           for _ in range(3)]
+    dit_qkv_epilogue(out[0], out[1], out[2], img_q, img_k, img_v, img_q.shape[0], img_stride,
+                     txt_q, txt_k, txt_v, txt_q.shape[0], txt_stride, img_q_w, img_k_w,
+                     txt_q_w, txt_k_w, img_cos, img_sin, txt_cos, txt_sin, heads, head_dim,
+                     img_eps, txt_eps)
+    return tuple(out)
+
+
+def bias_mul_add(x, bias, gate, residual):
+    """y = (x + bias) * gate + residual with one bf16 rounding of the multiply-add."""
+    for t, n in ((x, "x"), (gate, "gate"), (residual, "residual")):
+        _dense_bf16(t, n)
+    if bias is not None:
+        _dense_bf16(bias, "bias")
+    hidden = x.shape[-1]
+    y = torch.empty_like(x)
+    dit_bias_mul_add(y, x, bias, gate, residual, x.numel() // hidden, hidden)
+    return y
+
+
+def token_cat_quant(kind: int, a: torch.Tensor, b: torch.Tensor | None,
+                    scale: torch.Tensor):
+    """Quantise the row concatenation [a | b]. FP8: returns the E4M3 bytes
+    [rows, cols]. FP4: returns (packed [rows, cols/2], scales
+    [round_up(rows, 128), cols/16]); `scale` is then the global inverse scale."""
+    _dense_bf16(a, "a")
+    if b is not None:
+        _dense_bf16(b, "b")
+    _scalar_f32(scale, "scale")
+    rows, a_cols = a.shape
+    b_cols = 0 if b is None else b.shape[1]
+    cols = a_cols + b_cols
+    if kind == DIT_QUANT_FP8_E4M3:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=a.device)
+        dit_token_cat_quant(kind, out, None, a, a_cols, b, b_cols, rows, scale)
+        return out
+    packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device=a.device)
+    scales = torch.empty(((rows + 127) // 128 * 128, cols // 16), dtype=torch.uint8,
+                         device=a.device)
+    dit_token_cat_quant(kind, packed, scales, a, a_cols, b, b_cols, rows, scale)
+    return packed, scales

@@ -1,0 +1,149 @@
+// dit_device.h -- device-side helpers shared by the gfx950 epilogue kernels:
+// bf16 / FP8 / FP4 conversions, the exactly-rounded sums the epilogues need,
+// and wave64 reductions.
+//
+// Conversions use the gfx950 conversion instructions. Each one was checked
+// exhaustively over all 2^32 fp32 inputs against software encoders written
+// from the format definitions (round to nearest even; sign kept on zero):
+//   v_cvt_pk_bf16_f32          fp32 -> bf16
+//   v_cvt_pk_fp8_f32           fp32 in [-448, 448] -> OCP E4M3FN
+//   v_cvt_scalef32_pk_fp4_f32  fp32 -> E2M1 with unit scale (saturates at 6;
+//                              first source in the low nibble)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes: 8 bf16
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // 8 bytes
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+// Streaming stores: the outputs are not re-read by the kernel.
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store8(void* p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store4(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
+// ---- bf16 ------------------------------------------------------------------
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> two bf16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// 8 bf16 held in 16 bytes <-> 8 floats.
+__device__ __forceinline__ void unpack8(const u32x4& v, float (&f)[8]) {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
+    f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z);
+    f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+    return (u32x4){pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]),
+                   pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])};
+}
+
+// bf16 of the EXACT sum p + r of two fp32 values (one rounding). The fp32 sum
+// s = RN32(p + r) already rounds correctly to bf16 unless s lands exactly on
+// a bf16 midpoint (rounding is monotone and midpoints are fp32 values); then
+// the TwoSum error term says on which side the exact sum lies.
+__device__ __forceinline__ uint32_t bf16_bits_exact_sum(float p, float r) {
+    const float s = p + r;
+    const uint32_t u = __float_as_uint(s);
+    if (__builtin_expect((u & 0xFFFFu) == 0x8000u, 0)) {
+        const float bv = s - p;
+        const float e = (p - (s - bv)) + (r - bv);
+        if (e != 0.0f) return (u >> 16) + (((e > 0.0f) == (s > 0.0f)) ? 1u : 0u);
+    }
+    return pack_bf16(s, s) & 0xFFFFu;
+}
+
+// bf16 (round to nearest even) of a binary64 value, via fp32: RN32 cannot move
+// a value across a bf16 midpoint, only onto one, and that case is settled by
+// comparing with the binary64 value.
+__device__ __forceinline__ uint32_t bf16_bits_from_f64(double d) {
+    const float f = (float)d;
+    const uint32_t u = __float_as_uint(f);
+    if (__builtin_expect((u & 0xFFFFu) == 0x8000u, 0)) {
+        const double back = (double)f;
+        if (d != back) return (u >> 16) + (__builtin_fabs(d) > __builtin_fabs(back) ? 1u : 0u);
+    }
+    return pack_bf16(f, f) & 0xFFFFu;
+}
+
+// ---- FP8 E4M3FN ------------------------------------------------------------
+
+__device__ __forceinline__ float clamp_e4m3(float v) {
+    return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+
+// Four values already clamped to [-448, 448] -> four E4M3 bytes (a lowest).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Value of a non-negative E4M3FN code (sign bit clear, not NaN).
+__device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
+    const uint32_t e = c >> 3, m = c & 7u;
+    return e ? __builtin_ldexpf((float)(8u + m), (int)e - 10)
+             : __builtin_ldexpf((float)m, -9);
+}
+
+// ---- FP4 E2M1 ----------------------------------------------------------------
+
+// Eight values -> eight E2M1 nibbles in one dword (element 0 in the low nibble).
+__device__ __forceinline__ uint32_t pack_e2m1x8(const float (&t)[8]) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[0], t[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[2], t[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[4], t[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[6], t[7], 1.0f, 3);
+    return w;
+}
+
+// ---- wave64 reductions --------------------------------------------------------
+
+// DPP move of a 64-bit value (both halves with the same lane pattern).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+// Sum over each 16-lane row; every lane of the row gets the same bits.
+// quad_perm [1,0,3,2] and [2,3,0,1] sum a quad, row_half_mirror pairs the two
+// quads of each 8 lanes, row_mirror the two halves of the row.
+__device__ __forceinline__ double row16_sum(double v) {
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    return v;
+}
+
+// Sum over the whole wave64; every lane gets the same bits.
+__device__ __forceinline__ double wave_sum(double v) {
+    v = row16_sum(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+}  // namespace dit

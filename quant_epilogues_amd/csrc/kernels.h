@@ -1,0 +1,72 @@
+// kernels.h -- argument blocks and launchers of the gfx950 epilogue kernels.
+// Internal to libdit_epilogues: the C ABI (api.cpp) validates arguments on the
+// host and then calls one launcher, which only enqueues work on the stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// LayerNorm + AdaLN modulation + static FP8 (optionally after bias + gated
+// residual). residual == nullptr selects the plain variant.
+struct NormModulateArgs {
+    uint16_t* y;             // [rows, hidden] bf16
+    uint8_t* q;              // [rows, hidden] e4m3
+    uint16_t* r_out;         // [rows, hidden] bf16 (residual variant only)
+    const uint16_t* x;       // [rows, hidden]
+    const uint16_t* residual;  // [rows, hidden] or nullptr
+    const uint16_t* bias;    // [hidden] or nullptr
+    const uint16_t* gate;    // [hidden] (residual variant only)
+    const uint16_t* scale;   // [hidden]
+    const uint16_t* shift;   // [hidden]
+    const float* input_scale;  // device scalar
+    int64_t rows;
+    int32_t hidden;          // multiple of 8, <= kMaxHidden
+    float eps;
+};
+constexpr int kMaxHidden = 6144;
+hipError_t launch_norm_modulate_fp8(const NormModulateArgs& a, hipStream_t stream);
+
+struct QkvArgs {
+    uint16_t* joint[3];            // q, k, v outputs [txt + img, heads, 128]
+    const uint16_t* img[3];        // strided views
+    const uint16_t* txt[3];
+    const uint16_t* img_w[2];      // q, k RMSNorm weights [128]
+    const uint16_t* txt_w[2];
+    const float* img_cos;
+    const float* img_sin;
+    const float* txt_cos;
+    const float* txt_sin;
+    int64_t img_rows, img_stride;  // stride in elements
+    int64_t txt_rows, txt_stride;
+    int32_t heads;
+    float img_eps, txt_eps;
+};
+constexpr int kHeadDim = 128;
+constexpr int kMaxHeads = 64;
+hipError_t launch_qkv_epilogue(const QkvArgs& a, hipStream_t stream);
+
+struct BiasMulAddArgs {
+    uint16_t* y;
+    const uint16_t* x;
+    const uint16_t* bias;  // nullptr: no bias
+    const uint16_t* gate;
+    const uint16_t* residual;
+    int64_t rows;
+    int64_t hidden;        // multiple of 8
+};
+hipError_t launch_bias_mul_add(const BiasMulAddArgs& a, hipStream_t stream);
+
+struct TokenCatArgs {
+    uint8_t* out;
+    uint8_t* out_scales;   // FP4 only
+    const uint16_t* a;
+    const uint16_t* b;
+    int64_t a_cols, b_cols, rows;
+    const float* scale;    // device scalar
+};
+hipError_t launch_token_cat_fp8(const TokenCatArgs& a, hipStream_t stream);
+hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream);
+
+}  // namespace dit

@@ -1,0 +1,159 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and refuses bad arguments on the host before any HIP call.
+
+Only refusals and rows == 0 calls are made here (both return before touching
+HIP), with fake but aligned device addresses. The module is skipped where a GPU
+is visible so that no fake address can ever reach a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_visible() -> bool:
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only refusal tests use fake device addresses")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+FAKE2 = FAKE + 0x100000
+
+
+@pytest.fixture(scope="module")
+def native():
+    from quant_epilogues_amd import _native
+
+    if not os.path.exists(_native.LIB_PATH):
+        from quant_epilogues_amd import _build
+
+        _build.build()
+    _native.lib()
+    return _native
+
+
+def test_exports_every_declared_symbol(native):
+    declared = native.header_symbols()
+    assert set(declared) == {
+        "dit_abi_version", "dit_status_string", "dit_last_error", "dit_norm_modulate_fp8",
+        "dit_scale_residual_norm_modulate_fp8", "dit_qkv_epilogue", "dit_bias_mul_add",
+        "dit_token_cat_quant",
+    }
+    raw = ctypes.CDLL(native.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_strings(native):
+    L = native.lib()
+    with open(os.path.join(ROOT, "include", "dit_epilogues.h")) as f:
+        ver = int(re.search(r"#define DIT_ABI_VERSION (\d+)", f.read()).group(1))
+    assert L.dit_abi_version() == ver
+    names = [native.status_string(s) for s in range(6)]
+    assert names == ["DIT_OK", "DIT_ERR_NULL", "DIT_ERR_SHAPE", "DIT_ERR_ALIGN",
+                     "DIT_ERR_UNSUPPORTED", "DIT_ERR_HIP"]
+    assert native.status_string(99) == "DIT_ERR_UNKNOWN"
+
+
+def _nm(L, **kw):
+    a = dict(y=FAKE, q=FAKE, x=FAKE, scale=FAKE, shift=FAKE, s=FAKE, rows=4, hidden=3072, eps=1e-6)
+    a.update(kw)
+    return L.dit_norm_modulate_fp8(a["y"], a["q"], a["x"], a["scale"], a["shift"], a["s"],
+                                   a["rows"], a["hidden"], a["eps"], None)
+
+
+def test_norm_modulate_refusals(native):
+    L = native.lib()
+    assert _nm(L, y=None) == native.DIT_ERR_NULL
+    assert "NULL" in native.last_error()
+    assert _nm(L, rows=-1) == native.DIT_ERR_SHAPE
+    assert _nm(L, hidden=0) == native.DIT_ERR_SHAPE
+    assert _nm(L, hidden=3076) == native.DIT_ERR_UNSUPPORTED
+    assert _nm(L, hidden=6152) == native.DIT_ERR_UNSUPPORTED
+    assert _nm(L, x=FAKE + 2) == native.DIT_ERR_ALIGN
+    assert _nm(L, q=FAKE + 8) == native.DIT_ERR_ALIGN
+    assert _nm(L, s=FAKE + 2) == native.DIT_ERR_ALIGN
+    assert _nm(L, rows=0) == native.DIT_OK  # no-op, no HIP call
+    assert native.last_error() == ""
+
+
+def test_scale_residual_refusals(native):
+    L = native.lib()
+    f = L.dit_scale_residual_norm_modulate_fp8
+    args = [FAKE] * 10 + [4, 3072, 1e-6, None]
+    bad = list(args)
+    bad[0] = None
+    assert f(*bad) == native.DIT_ERR_NULL
+    bad = list(args)
+    bad[4] = FAKE + 4  # misaligned bias
+    assert f(*bad) == native.DIT_ERR_ALIGN
+    bad = list(args)
+    bad[4] = None  # bias is optional
+    bad[10] = 0
+    assert f(*bad) == native.DIT_OK
+    bad = list(args)
+    bad[11] = 12
+    assert f(*bad) == native.DIT_ERR_UNSUPPORTED
+
+
+def _qkv(L, **kw):
+    a = dict(heads=24, head_dim=128, img_rows=8, txt_rows=2, img_stride=9216, txt_stride=9216,
+             img_q=FAKE, txt_q=FAKE, jq=FAKE, img_cos=FAKE)
+    a.update(kw)
+    return L.dit_qkv_epilogue(a["jq"], FAKE, FAKE, a["img_q"], FAKE, FAKE, a["img_rows"],
+                              a["img_stride"], a["txt_q"], FAKE, FAKE, a["txt_rows"],
+                              a["txt_stride"], FAKE, FAKE, FAKE, FAKE, a["img_cos"], FAKE, FAKE,
+                              FAKE, a["heads"], a["head_dim"], 1e-6, 1e-6, None)
+
+
+def test_qkv_refusals(native):
+    L = native.lib()
+    assert _qkv(L, head_dim=64) == native.DIT_ERR_UNSUPPORTED  # only 128
+    assert _qkv(L, heads=0) == native.DIT_ERR_UNSUPPORTED
+    assert _qkv(L, heads=65) == native.DIT_ERR_UNSUPPORTED
+    assert _qkv(L, img_stride=3000) == native.DIT_ERR_SHAPE
+    assert _qkv(L, txt_stride=9220) == native.DIT_ERR_SHAPE
+    assert _qkv(L, img_rows=-1) == native.DIT_ERR_SHAPE
+    assert _qkv(L, jq=None) == native.DIT_ERR_NULL
+    assert _qkv(L, img_q=None) == native.DIT_ERR_NULL
+    assert _qkv(L, img_cos=FAKE + 4) == native.DIT_ERR_ALIGN
+    # A stream with no rows needs no pointers.
+    assert _qkv(L, img_rows=0, txt_rows=0, img_q=None, txt_q=None) == native.DIT_OK
+
+
+def test_bias_mul_add_refusals(native):
+    L = native.lib()
+    f = L.dit_bias_mul_add
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 4, 3072, None) == native.DIT_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3071, None) == native.DIT_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE + 2, FAKE, FAKE, 4, 3072, None) == native.DIT_ERR_ALIGN
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 0, 3072, None) == native.DIT_OK
+
+
+def test_token_cat_refusals(native):
+    L = native.lib()
+    f = L.dit_token_cat_quant
+    fp8, fp4 = native.DIT_QUANT_FP8_E4M3, native.DIT_QUANT_FP4_E2M1
+    assert f(7, FAKE, None, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_UNSUPPORTED
+    assert f(fp8, FAKE, None, FAKE, 6140, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_SHAPE
+    assert f(fp8, FAKE, None, FAKE, 0, FAKE2, 16, 4, FAKE, None) == native.DIT_ERR_SHAPE
+    assert f(fp4, FAKE, None, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_NULL
+    assert f(fp8, FAKE, None, FAKE, 6144, None, 18432, 4, FAKE, None) == native.DIT_ERR_NULL
+    assert f(fp8, FAKE + 8, None, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_ALIGN
+    assert f(fp4, FAKE, FAKE, FAKE, 6144, None, 0, 0, FAKE, None) == native.DIT_OK
+
+
+def test_python_binding_has_no_cpu_path(native):
+    import torch
+
+    import quant_epilogues_amd as qe
+
+    x = torch.zeros(4, 3072, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qe.norm_modulate_fp8(x, x[0], x[0], torch.ones(1), 1e-6)

@@ -1,0 +1,375 @@
+"""GPU parity: every entry point of libdit_epilogues against the CPU oracle.
+
+Inputs come from `synth` (seeded), the same bytes go to the oracle and to the
+GPU, and the outputs are compared with the tolerance rules in parity.py.
+Sizes cover the full workload shapes (512 text + 4096 image tokens, hidden
+3072, 24 heads; FLUX.2 rows of 6144 + 18432) and small ragged cases: partial
+waves and workgroups, hidden sizes that are not multiples of 512, heads not
+multiples of 4 and above 24, pad rows of the FP4 scale matrix. Outputs sit
+between guard bytes that must survive every call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import check_bf16, check_exact, check_fp4, check_fp8
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096  # bytes on each side of every output buffer
+
+
+@pytest.fixture(scope="module")
+def qe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import quant_epilogues_amd as qe_mod
+
+    qe_mod.lib()  # raises if the HIP library is not built
+    return qe_mod
+
+
+@pytest.fixture(scope="module")
+def e4m3_table(oracle_mod):
+    return oracle_mod.e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
+class Guarded:
+    """A device output tensor framed by canary bytes."""
+
+    def __init__(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.n = n
+        self.buf = torch.full((n + 2 * GUARD,), 0xA5, dtype=torch.uint8, device="cuda")
+        self.t = self.buf[GUARD:GUARD + n].view(dtype).view(shape)
+
+    def check(self, name):
+        head = self.buf[:GUARD].cpu().numpy()
+        tail = self.buf[GUARD + self.n:].cpu().numpy()
+        assert np.all(head == 0xA5) and np.all(tail == 0xA5), f"{name}: write outside its buffer"
+
+    def bits(self):
+        t = self.t.cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+
+def dev(t):
+    return t.cuda() if t is not None else None
+
+
+def dscalar(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def bits(t):
+    return synth.bf16_bits(t)
+
+
+def _print_case(*args):
+    print("case:", *args, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm + modulation + FP8
+# ---------------------------------------------------------------------------
+
+NORM_CASES = [
+    (127, 3072, 0.0625, 0),   # the small Qwen-Image case
+    (1, 3072, 0.4754464328, 1),
+    (1024, 3072, 0.02, 2),
+    (4096, 3072, 0.5, 3),     # full image-token count
+    (33, 512, 0.0625, 4),
+    (17, 1000, 0.0625, 5),    # ragged: 125 chunks over 64 lanes
+    (9, 6144, 0.02, 6),       # FLUX.2 width, 12 chunks per lane
+    (5, 8, 0.0625, 7),        # one chunk per row
+]
+
+
+@pytest.mark.parametrize("rows,hidden,input_scale,seed", NORM_CASES)
+def test_norm_modulate_fp8(qe, oracle_mod, e4m3_table, rows, hidden, input_scale, seed):
+    _print_case("norm_modulate_fp8", rows, hidden, input_scale, seed)
+    inp = synth.norm_modulate_inputs(rows, hidden, seed=seed, input_scale=input_scale)
+    y = Guarded((rows, hidden), torch.bfloat16)
+    q = Guarded((rows, hidden), torch.uint8)
+    qe.dit_norm_modulate_fp8(y.t, q.t, dev(inp.x), dev(inp.scale), dev(inp.shift),
+                             dscalar(inp.input_scale), rows, hidden, inp.eps)
+    torch.cuda.synchronize()
+    y.check("y"), q.check("q")
+    ry, rq, pre = oracle_mod.norm_modulate_fp8(bits(inp.x), bits(inp.scale), bits(inp.shift),
+                                               inp.input_scale, inp.eps)
+    ey = check_bf16("y", y.bits(), ry)
+    eq = check_fp8("q", q.bits(), rq, pre, e4m3_table)
+    print(f"exact: y {ey:.6f} q {eq:.6f}")
+
+
+SR_CASES = [
+    (4096, 3072, 0.02, True, 0),
+    (4096, 3072, 0.0625, True, 1),
+    (4096, 3072, 0.5, True, 2),
+    (4096, 3072, 0.0625, False, 3),
+    (127, 3072, 0.0625, True, 4),
+    (13, 1000, 0.02, True, 5),
+    (6, 6144, 0.5, False, 6),
+]
+
+
+@pytest.mark.parametrize("rows,hidden,input_scale,with_bias,seed", SR_CASES)
+def test_scale_residual_norm_modulate_fp8(qe, oracle_mod, e4m3_table, rows, hidden,
+                                          input_scale, with_bias, seed):
+    _print_case("scale_residual", rows, hidden, input_scale, with_bias, seed)
+    inp = synth.scale_residual_inputs(rows, hidden, seed=seed, input_scale=input_scale,
+                                      with_bias=with_bias)
+    r = Guarded((rows, hidden), torch.bfloat16)
+    y = Guarded((rows, hidden), torch.bfloat16)
+    q = Guarded((rows, hidden), torch.uint8)
+    qe.dit_scale_residual_norm_modulate_fp8(
+        r.t, y.t, q.t, dev(inp.x), dev(inp.bias), dev(inp.gate), dev(inp.residual),
+        dev(inp.scale), dev(inp.shift), dscalar(inp.input_scale), rows, hidden, inp.eps)
+    torch.cuda.synchronize()
+    for o, n in ((r, "r"), (y, "y"), (q, "q")):
+        o.check(n)
+    rr, ry, rq, pre = oracle_mod.scale_residual_norm_modulate_fp8(
+        bits(inp.x), None if inp.bias is None else bits(inp.bias), bits(inp.gate),
+        bits(inp.residual), bits(inp.scale), bits(inp.shift), inp.input_scale, inp.eps)
+    er = check_bf16("residual_out", r.bits(), rr)
+    ey = check_bf16("y", y.bits(), ry)
+    eq = check_fp8("q", q.bits(), rq, pre, e4m3_table)
+    print(f"exact: r {er:.6f} y {ey:.6f} q {eq:.6f}")
+
+
+def test_fp8_split_equals_fused_on_gpu(qe):
+    """q of the fused kernel == y re-quantised by the token-cat FP8 path."""
+    inp = synth.norm_modulate_inputs(256, 3072, seed=21, input_scale=0.4754464328)
+    s = dscalar(inp.input_scale)
+    y, q = qe.norm_modulate_fp8(dev(inp.x), dev(inp.scale), dev(inp.shift), s, inp.eps)
+    q2 = qe.token_cat_quant(qe.DIT_QUANT_FP8_E4M3, y, None, s)
+    torch.cuda.synchronize()
+    assert torch.equal(q.cpu(), q2.cpu())
+
+
+# ---------------------------------------------------------------------------
+# QKV epilogue
+# ---------------------------------------------------------------------------
+
+QKV_CASES = [
+    (4096, 512, 24, 0),   # Qwen-Image 1024^2: 4096 image + 512 text tokens
+    (5, 3, 3, 1),         # heads not a multiple of 4
+    (7, 2, 24, 2),
+    (3, 4, 48, 3),        # FLUX.2 head count: two 24-head blocks
+    (2, 1, 64, 4),
+    (6, 0, 24, 5),        # image only
+    (0, 5, 5, 6),         # text only
+]
+
+
+def _run_qkv(qe, inp, contiguous=False):
+    views = {}
+    for stream in ("img", "txt"):
+        qkv = dev(inp.img_qkv if stream == "img" else inp.txt_qkv)
+        q, k, v = inp.width, 2 * inp.width, 3 * inp.width
+        vs = (qkv[:, 0:q], qkv[:, q:k], qkv[:, k:v])
+        if contiguous:
+            vs = tuple(t.contiguous() for t in vs)
+        views[stream] = vs
+    n = inp.img_qkv.shape[0] + inp.txt_qkv.shape[0]
+    outs = [Guarded((n, inp.heads, inp.head_dim), torch.bfloat16) for _ in range(3)]
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    (iq, ik, iv), (tq, tk, tv) = views["img"], views["txt"]
+    qe.dit_qkv_epilogue(outs[0].t, outs[1].t, outs[2].t, iq, ik, iv, iq.shape[0], iq.stride(0),
+                        tq, tk, tv, tq.shape[0], tq.stride(0), dev(inp.img_q_w),
+                        dev(inp.img_k_w), dev(inp.txt_q_w), dev(inp.txt_k_w), f32(inp.img_cos),
+                        f32(inp.img_sin), f32(inp.txt_cos), f32(inp.txt_sin), inp.heads,
+                        inp.head_dim, inp.img_eps, inp.txt_eps)
+    torch.cuda.synchronize()
+    for o, name in zip(outs, "qkv"):
+        o.check("joint_" + name)
+    return [o.bits() for o in outs]
+
+
+@pytest.mark.parametrize("img_rows,txt_rows,heads,seed", QKV_CASES)
+def test_qkv_epilogue(qe, oracle_mod, img_rows, txt_rows, heads, seed):
+    _print_case("qkv_epilogue", img_rows, txt_rows, heads, seed)
+    inp = synth.qkv_inputs(img_rows, txt_rows, heads, 128, seed=seed, img_eps=1e-6,
+                           txt_eps=1e-5)
+    gq, gk, gv = _run_qkv(qe, inp)
+    rq, rk, rv = oracle_mod.qkv_epilogue_packed(
+        bits(inp.img_qkv), bits(inp.txt_qkv), bits(inp.img_q_w), bits(inp.img_k_w),
+        bits(inp.txt_q_w), bits(inp.txt_k_w), inp.img_cos, inp.img_sin, inp.txt_cos,
+        inp.txt_sin, inp.heads, inp.head_dim, inp.img_eps, inp.txt_eps)
+    eq = check_bf16("joint_q", gq, rq)
+    ek = check_bf16("joint_k", gk, rk)
+    check_exact("joint_v", gv, rv)
+    print(f"exact: q {eq:.6f} k {ek:.6f}")
+
+
+def test_qkv_contiguous_equals_strided(qe):
+    inp = synth.qkv_inputs(64, 16, 24, 128, seed=9)
+    a = _run_qkv(qe, inp, contiguous=False)
+    b = _run_qkv(qe, inp, contiguous=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# bias_mul_add
+# ---------------------------------------------------------------------------
+
+BMA_CASES = [
+    (4608, 3072, True, 0),   # 512 text + 4096 image tokens
+    (4608, 3072, False, 1),
+    (3, 1000, True, 2),
+    (5, 6144, True, 3),
+    (1, 8, True, 4),
+    (2, 25600, True, 5),     # a row longer than one unrolled step
+]
+
+
+@pytest.mark.parametrize("rows,hidden,with_bias,seed", BMA_CASES)
+def test_bias_mul_add(qe, oracle_mod, rows, hidden, with_bias, seed):
+    _print_case("bias_mul_add", rows, hidden, with_bias, seed)
+    inp = synth.bias_mul_add_inputs(rows, hidden, seed=seed, with_bias=with_bias)
+    y = Guarded((rows, hidden), torch.bfloat16)
+    qe.dit_bias_mul_add(y.t, dev(inp.x), dev(inp.bias), dev(inp.gate), dev(inp.residual),
+                        rows, hidden)
+    torch.cuda.synchronize()
+    y.check("y")
+    ry = oracle_mod.bias_mul_add(bits(inp.x), None if inp.bias is None else bits(inp.bias),
+                                 bits(inp.gate), bits(inp.residual))
+    print(f"exact: y {check_bf16('y', y.bits(), ry):.6f}")
+
+
+def test_bias_mul_add_tie_case(qe, oracle_mod):
+    """The tie-guard inputs of the output-bias-absorption page, on the GPU."""
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "bias_mul_add_tie.json")) as f:
+        c = json.load(f)["inputs"]
+    H = 8
+    t = lambda v: torch.full((1, H), v, dtype=torch.bfloat16)
+    x, res = t(c["x"]), t(c["residual"])
+    bias, gate = t(c["bias"])[0], t(c["gate"])[0]
+    y = qe.bias_mul_add(dev(x), dev(bias), dev(gate), dev(res))
+    ry = oracle_mod.bias_mul_add(bits(x), bits(bias), bits(gate), bits(res))
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ry)
+
+
+# ---------------------------------------------------------------------------
+# Token concatenation + FP8 / FP4
+# ---------------------------------------------------------------------------
+
+def _sample_rows(rows, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [r for r in (0, 1, 2, 127, 128, 2047, 2048, rows - 2, rows - 1) if 0 <= r < rows]
+    return np.unique(np.concatenate([fixed, rng.integers(0, rows, 24)])).astype(np.int64)
+
+
+FP8_CASES = [
+    (4608, 6144, 18432, 0.05, 0, True),  # FLUX.2 single block, sampled rows
+    (7, 96, 160, 0.05, 1, False),
+    (3, 6144, 0, 0.5, 2, False),
+    (130, 16, 48, 0.4754464328, 3, False),
+]
+
+
+@pytest.mark.parametrize("rows,a_cols,b_cols,scale,seed,sample", FP8_CASES)
+def test_token_cat_fp8(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, scale, seed, sample):
+    _print_case("token_cat_fp8", rows, a_cols, b_cols, scale, seed)
+    inp = synth.token_cat_inputs(rows, a_cols, b_cols, seed=seed, fp8_scale=scale)
+    cols = a_cols + b_cols
+    out = Guarded((rows, cols), torch.uint8)
+    qe.dit_token_cat_quant(qe.DIT_QUANT_FP8_E4M3, out.t, None, dev(inp.attn), a_cols,
+                           dev(inp.mlp) if b_cols else None, b_cols, rows, dscalar(inp.fp8_scale))
+    torch.cuda.synchronize()
+    out.check("out")
+    sel = _sample_rows(rows, seed) if sample else np.arange(rows)
+    a_b, m_b = bits(inp.attn)[sel], bits(inp.mlp)[sel]
+    rq, pre = oracle_mod.token_cat_fp8(a_b, m_b, inp.fp8_scale)
+    print(f"exact: q {check_fp8('q', out.bits()[sel], rq, pre, e4m3_table):.6f}")
+
+
+@pytest.mark.parametrize("inv_scale", [1.0, 16.0, 50.0, 20.0, 2.0, 1.0 / 0.4754464328])
+def test_token_cat_fp8_all_bf16_values(qe, oracle_mod, inv_scale):
+    """Every finite bf16 pattern through the FP8 path, at each scale."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[(pats & 0x7F80) != 0x7F80]
+    pats = np.concatenate([pats, np.zeros((-pats.size) % 4096, np.uint16)]).reshape(-1, 4096)
+    a = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16)
+    scale = float(np.float32(1.0) / np.float32(inv_scale))
+    q = qe.token_cat_quant(qe.DIT_QUANT_FP8_E4M3, dev(a), None, dscalar(scale))
+    rq, _ = oracle_mod.token_cat_fp8(pats, np.zeros((pats.shape[0], 0), np.uint16), scale)
+    check_exact("q", q.cpu().numpy(), rq)
+
+
+FP4_CASES = [
+    (4608, 6144, 18432, "calibrated", 0, True),
+    (17, 64, 192, "calibrated", 1, False),   # 111 pad rows in the scale matrix
+    (9, 32, 32, 1.0, 2, False),
+    (9, 32, 32, 1e4, 3, False),              # saturating scales
+    (128, 6144, 0, "calibrated", 4, False),
+    (129, 16, 16, "calibrated", 5, False),
+]
+
+
+@pytest.mark.parametrize("rows,a_cols,b_cols,g,seed,sample", FP4_CASES)
+def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed, sample):
+    _print_case("token_cat_fp4", rows, a_cols, b_cols, g, seed)
+    inp = synth.token_cat_inputs(rows, a_cols, b_cols, seed=seed)
+    gv = inp.fp4_g if g == "calibrated" else float(np.float32(g))
+    cols = a_cols + b_cols
+    rows_pad = (rows + 127) // 128 * 128
+    packed = Guarded((rows, cols // 2), torch.uint8)
+    scales = Guarded((rows_pad, cols // 16), torch.uint8)
+    qe.dit_token_cat_quant(qe.DIT_QUANT_FP4_E2M1, packed.t, scales.t, dev(inp.attn), a_cols,
+                           dev(inp.mlp) if b_cols else None, b_cols, rows, dscalar(gv))
+    torch.cuda.synchronize()
+    packed.check("packed"), scales.check("scales")
+    gp, gs = packed.bits(), scales.bits()
+    sel = _sample_rows(rows, seed) if sample else np.arange(rows)
+    a_b, m_b = bits(inp.attn)[sel], bits(inp.mlp)[sel]
+    rp, rs, s_pre, pre = oracle_mod.token_cat_fp4(a_b, m_b, gv)
+    x = oracle_mod.f32_from_bf16(np.concatenate([a_b, m_b], axis=1))
+    gs_sel = np.concatenate([gs[sel], gs[rows:]])
+    rs_full = np.concatenate([rs[:len(sel)], np.zeros((rows_pad - rows, cols // 16), np.uint8)])
+    ec, es = check_fp4("fp4", gp[sel], gs_sel, rp, rs_full, s_pre, pre, x, gv, e4m3_table,
+                       oracle_mod.e2m1_encode)
+    print(f"exact: codes {ec:.6f} scales {es:.6f}")
+
+
+# ---------------------------------------------------------------------------
+# Boundary behaviour on the device
+# ---------------------------------------------------------------------------
+
+def test_zero_rows_and_refusals_leave_outputs_untouched(qe):
+    y = Guarded((4, 3072), torch.bfloat16)
+    q = Guarded((4, 3072), torch.uint8)
+    x = torch.randn(4, 3072, device="cuda").to(torch.bfloat16)
+    sc = torch.zeros(3072, device="cuda", dtype=torch.bfloat16)
+    s = dscalar(0.0625)
+    before = y.buf.clone(), q.buf.clone()
+    qe.dit_norm_modulate_fp8(y.t, q.t, x, sc, sc, s, 0, 3072, 1e-6)  # rows == 0: no-op
+    with pytest.raises(qe.DitError) as e:  # 2-byte offset: refused
+        qe.dit_norm_modulate_fp8(y.t, q.t, x.view(-1)[1:].data_ptr(), sc, sc, s, 3, 3072, 1e-6)
+    assert e.value.status == qe.DIT_ERR_ALIGN
+    with pytest.raises(qe.DitError) as e:
+        qe.dit_norm_modulate_fp8(y.t, q.t, x, sc, sc, s, 4, 3076, 1e-6)
+    assert e.value.status == qe.DIT_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(y.buf, before[0]) and torch.equal(q.buf, before[1])
+
+
+def test_runs_on_a_side_stream(qe):
+    inp = synth.bias_mul_add_inputs(64, 3072, seed=12)
+    x, b, g, r = dev(inp.x), dev(inp.bias), dev(inp.gate), dev(inp.residual)
+    ref = qe.bias_mul_add(x, b, g, r)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out = qe.bias_mul_add(x, b, g, r)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, out)
