@@ -1,0 +1,353 @@
+"""Benchmark of the fused DiT-block epilogues on one MI355X.
+
+One step = one pass over every fused epilogue at its full workload shape:
+  norm_img   dit_norm_modulate_fp8                 [4096, 3072]  (image tokens)
+  norm_txt   dit_norm_modulate_fp8                 [512, 3072]   (text tokens)
+  qkv        dit_qkv_epilogue                      512 text + 4096 image tokens, 24 x 128
+  sr_norm    dit_scale_residual_norm_modulate_fp8  [4096, 3072] with bias
+  bma        dit_bias_mul_add                      [4608, 3072]
+  cat_fp8    dit_token_cat_quant FP8               [4608, 6144 + 18432]
+  cat_fp4    dit_token_cat_quant FP4               [4608, 6144 + 18432]
+Inputs are seeded synthetic tensors already resident in HBM; every launch has
+its own buffers, so one step touches about 1.3 GB and no kernel finds its
+inputs in the 256 MB Infinity Cache from the previous step.
+
+Bytes are compulsory bytes: every input read once, every output written once,
+row-broadcast vectors once. The printed JSON line reports the whole-step
+throughput (GB/s), per-kernel us/call and GB/s, the roofline entry of the
+kernel that takes the most time, and the CPU oracle timed on a row sample.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--blocks N]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+METRIC = "fused-epilogue HBM GB/s (% of MI355X peak) + µs/call at Qwen-Image shapes"
+
+QWEN_HIDDEN, IMG, TXT, HEADS, HEAD_DIM = 3072, 4096, 512, 24, 128
+FLUX_ROWS, FLUX_A, FLUX_B = 4608, 6144, 18432
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- compulsory bytes per launch ------------------------------------------------
+
+def bytes_norm(rows, hidden):
+    return 5 * rows * hidden + 4 * hidden + 4
+
+
+def bytes_sr(rows, hidden, bias=True):
+    return 9 * rows * hidden + (8 if bias else 6) * hidden + 4
+
+
+def bytes_qkv(n_tok, heads, head_dim):
+    return 12 * n_tok * heads * head_dim + 2 * 4 * n_tok * (head_dim // 2) + 4 * 2 * head_dim
+
+
+def bytes_bma(rows, hidden, bias=True):
+    return 6 * rows * hidden + (4 if bias else 2) * hidden
+
+
+def bytes_cat_fp8(rows, cols):
+    return 3 * rows * cols + 4
+
+
+def bytes_cat_fp4(rows, cols):
+    return 2 * rows * cols + rows * cols // 2 + (rows + 127) // 128 * 128 * (cols // 16) + 4
+
+
+# ---- workload ---------------------------------------------------------------------
+
+class Workload:
+    """Device buffers and the launch list of one step. `names` selects launches."""
+
+    ALL = ("norm_img", "norm_txt", "qkv", "sr_norm", "bma", "cat_fp8", "cat_fp4")
+
+    def __init__(self, torch, qe, seed=0, names=ALL):
+        import numpy as np
+
+        import synth
+
+        dev = torch.device("cuda:0")
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+
+        def randn(*shape, std=1.0, mean=0.0):
+            return (torch.randn(*shape, generator=g, device=dev) * std + mean).to(torch.bfloat16)
+
+        def empty(*shape, dtype=torch.bfloat16):
+            return torch.empty(*shape, dtype=dtype, device=dev)
+
+        def scalar(v):
+            return torch.tensor([v], dtype=torch.float32, device=dev)
+
+        H = QWEN_HIDDEN
+        W = HEADS * HEAD_DIM
+        C = FLUX_A + FLUX_B
+        s0625 = scalar(0.0625)
+        self.keep = []  # keeps every buffer alive; launches take raw device addresses
+        st = torch.cuda.current_stream(dev).cuda_stream
+
+        def P(*ts):
+            self.keep.extend(ts)
+            return [None if t is None else t.data_ptr() for t in ts]
+
+        def norm(rows):
+            x, sc, sh = randn(rows, H), randn(H, std=0.1), randn(H, std=0.1)
+            y, q = empty(rows, H), empty(rows, H, dtype=torch.uint8)
+            p = P(y, q, x, sc, sh, s0625)
+            return bytes_norm(rows, H), lambda: qe.dit_norm_modulate_fp8(
+                *p, rows, H, 1e-6, stream=st)
+
+        def qkv():
+            img, txt = randn(IMG, 3 * W), randn(TXT, 3 * W)
+            ws = [randn(HEAD_DIM, std=0.05, mean=1.0) for _ in range(4)]
+            tc, ts = synth.rope_tables(np.arange(TXT), HEAD_DIM)
+            ic, is_ = synth.rope_tables(np.arange(TXT, TXT + IMG), HEAD_DIM)
+            tc, ts, ic, is_ = (torch.from_numpy(a).to(dev) for a in (tc, ts, ic, is_))
+            jq, jk, jv = (empty(IMG + TXT, HEADS, HEAD_DIM) for _ in range(3))
+            o = P(jq, jk, jv)
+            i3 = P(img[:, :W], img[:, W:2 * W], img[:, 2 * W:])
+            t3 = P(txt[:, :W], txt[:, W:2 * W], txt[:, 2 * W:])
+            w4 = P(*ws)
+            r4 = P(ic, is_, tc, ts)
+            return bytes_qkv(IMG + TXT, HEADS, HEAD_DIM), lambda: qe.dit_qkv_epilogue(
+                *o, *i3, IMG, 3 * W, *t3, TXT, 3 * W, *w4, *r4, HEADS, HEAD_DIM, 1e-6, 1e-6,
+                stream=st)
+
+        def sr_norm():
+            x, res = randn(IMG, H), randn(IMG, H)
+            b, gt = randn(H, std=0.02), randn(H, std=0.1, mean=1.0)
+            sc, sh = randn(H, std=0.1), randn(H, std=0.1)
+            r, y, q = empty(IMG, H), empty(IMG, H), empty(IMG, H, dtype=torch.uint8)
+            p = P(r, y, q, x, b, gt, res, sc, sh, s0625)
+            return bytes_sr(IMG, H), lambda: qe.dit_scale_residual_norm_modulate_fp8(
+                *p, IMG, H, 1e-6, stream=st)
+
+        def bma():
+            R = IMG + TXT
+            x, res = randn(R, H), randn(R, H)
+            b, gt = randn(H, std=0.02), randn(H, std=0.5)
+            y = empty(R, H)
+            p = P(y, x, b, gt, res)
+            return bytes_bma(R, H), lambda: qe.dit_bias_mul_add(*p, R, H, stream=st)
+
+        def cat(kind):
+            a, m = randn(FLUX_ROWS, FLUX_A), randn(FLUX_ROWS, FLUX_B)
+            if kind == qe.DIT_QUANT_FP8_E4M3:
+                out, scales, s = empty(FLUX_ROWS, C, dtype=torch.uint8), None, scalar(0.05)
+                nbytes = bytes_cat_fp8(FLUX_ROWS, C)
+            else:
+                out = empty(FLUX_ROWS, C // 2, dtype=torch.uint8)
+                scales = empty((FLUX_ROWS + 127) // 128 * 128, C // 16, dtype=torch.uint8)
+                amax = max(float(a.float().abs().max()), float(m.float().abs().max()))
+                s = scalar(float(np.float32(np.float32(2688.0) / np.float32(amax))))
+                nbytes = bytes_cat_fp4(FLUX_ROWS, C)
+            po, ps, pa, pm, pscale = P(out, scales, a, m, s)
+            return nbytes, lambda: qe.dit_token_cat_quant(kind, po, ps, pa, FLUX_A, pm, FLUX_B,
+                                                          FLUX_ROWS, pscale, stream=st)
+
+        builders = {
+            "norm_img": lambda: norm(IMG), "norm_txt": lambda: norm(TXT), "qkv": qkv,
+            "sr_norm": sr_norm, "bma": bma,
+            "cat_fp8": lambda: cat(qe.DIT_QUANT_FP8_E4M3),
+            "cat_fp4": lambda: cat(qe.DIT_QUANT_FP4_E2M1),
+        }
+        self.launches = []  # (name, compulsory bytes, launch)
+        for n in names:
+            nbytes, fn = builders[n]()
+            self.launches.append((n, nbytes, fn))
+        self.step_bytes = sum(b for _, b, _ in self.launches)
+
+    def step(self):
+        for _, _, fn in self.launches:
+            fn()
+
+
+def time_steps(torch, wl, steps, per_kernel):
+    """Outer-event timing of `steps` steps; with per_kernel, an event pair
+    around every launch (on torch's current stream, where the kernels run)."""
+    stream = torch.cuda.current_stream()
+    names = [n for n, _, _ in wl.launches]
+    pairs = {n: [] for n in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        for n, _, fn in wl.launches:
+            if per_kernel:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                pairs[n].append((e0, e1))
+            else:
+                fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    kern = {n: sorted(e0.elapsed_time(e1) for e0, e1 in pairs[n]) for n in names} if per_kernel else {}
+    return total_ms, wall, kern
+
+
+def cpu_baseline(sample_div=3):
+    """The CPU oracle, single-threaded, on a row sample of the same step."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    if not os.path.exists(oracle._LIB_PATH):
+        oracle.build()
+    H = QWEN_HIDDEN
+    img, txt, flux = IMG // sample_div, TXT // sample_div, FLUX_ROWS // sample_div
+    b = synth.bf16_bits
+    nm_i = synth.norm_modulate_inputs(img, H, seed=0)
+    nm_t = synth.norm_modulate_inputs(txt, H, seed=1)
+    qk = synth.qkv_inputs(img, txt, HEADS, HEAD_DIM, seed=2)
+    sr = synth.scale_residual_inputs(img, H, seed=3)
+    bm = synth.bias_mul_add_inputs(img + txt, H, seed=4)
+    tc = synth.token_cat_inputs(flux, FLUX_A, FLUX_B, seed=5)
+    args = dict(
+        nm_i=(b(nm_i.x), b(nm_i.scale), b(nm_i.shift)), nm_t=(b(nm_t.x), b(nm_t.scale), b(nm_t.shift)),
+        qk=(b(qk.img_qkv), b(qk.txt_qkv), b(qk.img_q_w), b(qk.img_k_w), b(qk.txt_q_w), b(qk.txt_k_w)),
+        sr=(b(sr.x), b(sr.bias), b(sr.gate), b(sr.residual), b(sr.scale), b(sr.shift)),
+        bm=(b(bm.x), b(bm.bias), b(bm.gate), b(bm.residual)), tc=(b(tc.attn), b(tc.mlp)))
+    t0 = time.perf_counter()
+    oracle.norm_modulate_fp8(*args["nm_i"], 0.0625, 1e-6)
+    oracle.norm_modulate_fp8(*args["nm_t"], 0.0625, 1e-6)
+    oracle.qkv_epilogue_packed(*args["qk"], qk.img_cos, qk.img_sin, qk.txt_cos, qk.txt_sin,
+                               HEADS, HEAD_DIM, 1e-6, 1e-6)
+    oracle.scale_residual_norm_modulate_fp8(*args["sr"], 0.0625, 1e-6)
+    oracle.bias_mul_add(*args["bm"])
+    oracle.token_cat_fp8(*args["tc"], 0.05)
+    oracle.token_cat_fp4(*args["tc"], tc.fp4_g)
+    secs = time.perf_counter() - t0
+    C = FLUX_A + FLUX_B
+    nbytes = (bytes_norm(img, H) + bytes_norm(txt, H) + bytes_qkv(img + txt, HEADS, HEAD_DIM)
+              + bytes_sr(img, H) + bytes_bma(img + txt, H) + bytes_cat_fp8(flux, C)
+              + bytes_cat_fp4(flux, C))
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"every epilogue of the step on 1/{sample_div} of its rows "
+                      f"({img} image + {txt} text tokens, {flux} FLUX.2 rows), single thread, "
+                      f"{secs:.1f} s"}
+
+
+def block_sequence(torch, qe, blocks, reps):
+    """Qwen-Image-shaped block sequence: per block norm-FP8 (image, text),
+    QKV epilogue, bias_mul_add, each block on its own random buffers."""
+    wls = [Workload(torch, qe, seed=100 + i, names=("norm_img", "norm_txt", "qkv", "bma"))
+           for i in range(blocks)]
+    for wl in wls:
+        wl.step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        for wl in wls:
+            wl.step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    nbytes = sum(wl.step_bytes for wl in wls)
+    return {"blocks": blocks, "launches": 4 * blocks, "bytes": nbytes, "ms_per_pass": round(ms, 4),
+            "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (each copy reads and writes `nbytes`)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_()
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": nbytes, "copies": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-sample-div", type=int, default=3,
+                    help="the CPU oracle runs on 1/N of each epilogue's rows")
+    ap.add_argument("--only", default="", help="comma-separated subset of launches to time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--blocks", type=int, default=0,
+                    help="also time a Qwen-Image block sequence of this many blocks (e.g. 60)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: these epilogues need no cross-GPU exchange and "
+              "this build runs on a single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quant_epilogues_amd as qe
+
+    qe.lib()
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    names = tuple(args.only.split(",")) if args.only else Workload.ALL
+    wl = Workload(torch, qe, seed=0, names=names)
+    for _ in range(args.warmup):
+        wl.step()
+    total_ms, wall, _ = time_steps(torch, wl, args.steps, per_kernel=False)
+    _, _, kern = time_steps(torch, wl, args.steps, per_kernel=True)
+    ms = total_ms / args.steps
+    value = wl.step_bytes / (ms * 1e-3) / 1e9
+
+    kernels = {}
+    for name, nbytes, _ in wl.launches:
+        t = kern[name]
+        mean = sum(t) / len(t)
+        kernels[name] = {"us_per_call": round(1e3 * mean, 3), "us_median": round(1e3 * t[len(t) // 2], 3),
+                         "bytes": nbytes, "gb_s": round(nbytes / (mean * 1e-3) / 1e9, 1),
+                         "pct_peak": round(100 * nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
+    achieved = kernels[dom]["gb_s"]
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded randn, resident in HBM)",
+        "config": {"workload": "Qwen-Image block epilogues (hidden 3072, 512 text + 4096 image "
+                               "tokens, 24x128 heads) + FLUX.2 single-block token-cat FP8/FP4 "
+                               "(4608 x 6144+18432)",
+                   "launches_per_step": len(wl.launches), "step_bytes": wl.step_bytes,
+                   "io": "bf16 in; bf16 + E4M3 / E2M1 out", "parallelism": "1 GPU"},
+        "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "kernels": kernels,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if args.blocks:
+        out["block_sequence"] = block_sequence(torch, qe, args.blocks, reps=3)
+    if not args.no_cpu:
+        log("timing the CPU oracle on a row sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_div)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -78,8 +78,8 @@ const char* dit_last_error(void);
  *   eps    LayerNorm epsilon (host fp32)
  *
  * Statistics: mean and biased variance per row; 1 / input_scale is IEEE fp32
- * division. hidden must be a multiple of 8 and at most 6144 (the row is held
- * in registers), else DIT_ERR_UNSUPPORTED.
+ * division. hidden must be a multiple of 8 and at most 8192 (one workgroup
+ * holds the row), else DIT_ERR_UNSUPPORTED.
  */
 int dit_norm_modulate_fp8(void* y, uint8_t* q, const void* x, const void* scale,
                           const void* shift, const float* input_scale_dev,

@@ -43,7 +43,7 @@ int launched(hipError_t e, const char* what) {
     return ok();
 }
 
-constexpr int64_t kMaxRows = int64_t(1) << 33;  // grid.x = rows / 4 stays below 2^31
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 128;  // one workgroup row per grid.x index
 
 }  // namespace
 
@@ -161,7 +161,7 @@ int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v, const void* im
         (txt_rows > 0 && (txt_row_stride < width || txt_row_stride % 8 != 0)))
         return fail(DIT_ERR_SHAPE, "%s: row strides must be >= heads*head_dim (%lld) and a multiple of 8",
                     fn, (long long)width);
-    const int64_t hblocks = (heads + 23) / 24;
+    const int64_t hblocks = (heads + dit::kQkvHeadsPerWave - 1) / dit::kQkvHeadsPerWave;
     if ((img_rows + txt_rows) * hblocks >= (int64_t(1) << 32) - 4)
         return fail(DIT_ERR_UNSUPPORTED, "%s: too many tokens", fn);
     const void* ptrs16[] = {joint_q, joint_k, joint_v};
@@ -244,7 +244,7 @@ int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales, const v
     if (a_cols % 16 != 0 || b_cols % 16 != 0 || a_cols < 16)
         return fail(DIT_ERR_SHAPE, "%s: a_cols (%lld) and b_cols (%lld) must be multiples of 16, a_cols >= 16",
                     fn, (long long)a_cols, (long long)b_cols);
-    if (a_cols + b_cols > (int64_t(1) << 30) || rows > kMaxRows)
+    if (a_cols + b_cols > (int64_t(1) << 28) || rows > kMaxRows)  // grid.y = cols / 4096 tiles
         return fail(DIT_ERR_UNSUPPORTED, "%s: shape too large", fn);
     if (!out || !a || !scale_dev || (b_cols > 0 && !b) ||
         (kind == DIT_QUANT_FP4_E2M1 && !out_scales))

@@ -8,40 +8,41 @@
 // product ties at large magnitudes.
 //
 // On gfx950 the product of two bf16 values is exact in fp32, so only the final
-// sum needs care: bf16_bits_exact_sum rounds p + residual once.
+// sum needs care: pack8_exact_sum rounds p + residual once.
 //
-// Layout: one wave64 per row; lane l handles 16-byte chunks l, l + 64, ...,
-// processed kUnroll chunks at a time so that 2 * kUnroll 16-byte loads per lane
-// are in flight. bias and gate are row-broadcast and stay in L2.
+// Layout: WPR waves per row and RPW rows per workgroup; wave w of a row takes
+// 16-byte chunks 64 (w + WPR k) + lane for k < V (rows wider than
+// 512 * WPR * V columns loop), so each instruction of a wave moves 1 KiB of
+// contiguous HBM. x and residual stream through with non-temporal loads;
+// bias and gate are row-broadcast and stay in L2.
 #include "dit_device.h"
 #include "kernels.h"
 
 namespace dit {
 namespace {
 
-constexpr int kUnroll = 6;
-
-template <bool kHasBias>
-__global__ __launch_bounds__(256) void bias_mul_add_kernel(BiasMulAddArgs a) {
+template <bool kHasBias, int WPR, int RPW, int V>
+__global__ __launch_bounds__(64 * WPR * RPW) void bias_mul_add_kernel(BiasMulAddArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
+    const int sw = wave % WPR;
+    const int64_t row = (int64_t)blockIdx.x * RPW + wave / WPR;
     if (row >= a.rows) return;
     const int cpr = (int)(a.hidden >> 3);
     const int64_t base = row * a.hidden;
-
-    for (int c0 = 0; c0 < cpr; c0 += 64 * kUnroll) {
-        u32x4 xv[kUnroll], rv[kUnroll];
+    for (int c0 = 0; c0 < cpr; c0 += 64 * WPR * V) {
+        u32x4 xv[V], rv[V];
 #pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int c = c0 + lane + 64 * k;
+        for (int k = 0; k < V; ++k) {
+            const int c = c0 + 64 * (sw + WPR * k) + lane;
             if (c < cpr) {
-                xv[k] = load16(a.x + base + 8 * c);
-                rv[k] = load16(a.residual + base + 8 * c);
+                xv[k] = stream_load16(a.x + base + 8 * c);
+                rv[k] = stream_load16(a.residual + base + 8 * c);
             }
         }
 #pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int c = c0 + lane + 64 * k;
+        for (int k = 0; k < V; ++k) {
+            const int c = c0 + 64 * (sw + WPR * k) + lane;
             if (c >= cpr) continue;
             float xf[8], rf[8], gf[8];
             unpack8(xv[k], xf);
@@ -57,27 +58,35 @@ __global__ __launch_bounds__(256) void bias_mul_add_kernel(BiasMulAddArgs a) {
                     xf[i + 1] = bf_hi(w);
                 }
             }
-            uint32_t yw[4];
+            float prod[8];
 #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const uint32_t lo = bf16_bits_exact_sum(xf[i] * gf[i], rf[i]);
-                const uint32_t hi = bf16_bits_exact_sum(xf[i + 1] * gf[i + 1], rf[i + 1]);
-                yw[i / 2] = lo | (hi << 16);
-            }
+            for (int i = 0; i < 8; ++i) prod[i] = xf[i] * gf[i];  // exact in fp32
+            uint32_t yw[4];
+            pack8_exact_sum(prod, rf, yw);
             store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
         }
     }
 }
 
+template <bool kHasBias, int WPR, int RPW, int V>
+hipError_t launch_geom(const BiasMulAddArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.rows + RPW - 1) / RPW));
+    hipLaunchKernelGGL((bias_mul_add_kernel<kHasBias, WPR, RPW, V>), grid, dim3(64 * WPR * RPW), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+// Six waves per row, one chunk per lane (measured best on MI355X at hidden
+// 3072: 384 chunks = one pass; wider rows loop).
+template <bool kHasBias>
+hipError_t launch_bias(const BiasMulAddArgs& a, hipStream_t stream) {
+    return launch_geom<kHasBias, 6, 1, 1>(a, stream);
+}
+
 }  // namespace
 
 hipError_t launch_bias_mul_add(const BiasMulAddArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.rows + 3) / 4));
-    if (a.bias)
-        hipLaunchKernelGGL(bias_mul_add_kernel<true>, grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(bias_mul_add_kernel<false>, grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return a.bias ? launch_bias<true>(a, stream) : launch_bias<false>(a, stream);
 }
 
 }  // namespace dit

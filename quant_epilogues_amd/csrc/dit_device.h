@@ -21,9 +21,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes: 8 bf16
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // 8 bytes
 
+// Cached loads: row-broadcast vectors (scale, shift, gate, bias, weights,
+// cos/sin) that many workgroups re-read from L2.
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
-// Streaming stores: the outputs are not re-read by the kernel.
+// Streaming loads and stores: tensors touched exactly once. The non-temporal
+// hint keeps them from displacing the broadcast vectors in L2 and measurably
+// raises sustained HBM bandwidth on gfx950.
+__device__ __forceinline__ u32x4 stream_load16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
@@ -56,32 +62,75 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
                    pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])};
 }
 
-// bf16 of the EXACT sum p + r of two fp32 values (one rounding). The fp32 sum
-// s = RN32(p + r) already rounds correctly to bf16 unless s lands exactly on
-// a bf16 midpoint (rounding is monotone and midpoints are fp32 values); then
-// the TwoSum error term says on which side the exact sum lies.
-__device__ __forceinline__ uint32_t bf16_bits_exact_sum(float p, float r) {
-    const float s = p + r;
-    const uint32_t u = __float_as_uint(s);
-    if (__builtin_expect((u & 0xFFFFu) == 0x8000u, 0)) {
-        const float bv = s - p;
-        const float e = (p - (s - bv)) + (r - bv);
-        if (e != 0.0f) return (u >> 16) + (((e > 0.0f) == (s > 0.0f)) ? 1u : 0u);
+// bf16 of the EXACT sums p[i] + r[i] of fp32 values (one rounding each), two
+// per word, element 2j in the low half of word j. The fp32 sum s = RN32(p + r)
+// already rounds correctly to bf16 unless s lands exactly on a bf16 midpoint
+// (rounding is monotone and bf16 midpoints are fp32 values) AND the fp32 sum
+// was inexact; then the TwoSum error term says on which side the exact sum
+// lies. For a bf16 product p and a bf16 r the fp32 sum is usually exact, and
+// exact sums sit on bf16 midpoints often (~1/256), so the test is two-level,
+// each level a wave-uniform branch: any midpoint (common), then any inexact
+// midpoint (rare). The sum is inexact iff s - p != r or s - r != p (whichever
+// operand is larger in magnitude, its difference with s is exact).
+__device__ __forceinline__ void pack8_exact_sum(const float (&p)[8], const float (&r)[8],
+                                                uint32_t (&w)[4]) {
+    float s[8];
+    bool mid = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s[i] = p[i] + r[i];
+        mid |= (__float_as_uint(s[i]) & 0xFFFFu) == 0x8000u;
     }
-    return pack_bf16(s, s) & 0xFFFFu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack_bf16(s[2 * j], s[2 * j + 1]);
+    if (__builtin_amdgcn_ballot_w64(mid) == 0) return;
+    uint32_t fix = 0;  // bitwise, branch-free: computed for all 8 values
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t m = (__float_as_uint(s[i]) & 0xFFFFu) == 0x8000u;
+        const uint32_t inexact = ((s[i] - p[i]) != r[i]) | ((s[i] - r[i]) != p[i]);
+        fix |= m & inexact;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(fix != 0) == 0, 1)) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t u = __float_as_uint(s[i]);
+        if ((u & 0xFFFFu) != 0x8000u) continue;
+        const float bv = s[i] - p[i];
+        const float e = (p[i] - (s[i] - bv)) + (r[i] - bv);
+        if (e == 0.0f) continue;  // an exact tie: the even choice stands
+        const uint32_t h = (u >> 16) + (((e > 0.0f) == (s[i] > 0.0f)) ? 1u : 0u);
+        const int sh = (i & 1) * 16;
+        w[i / 2] = (w[i / 2] & ~(0xFFFFu << sh)) | (h << sh);
+    }
 }
 
-// bf16 (round to nearest even) of a binary64 value, via fp32: RN32 cannot move
-// a value across a bf16 midpoint, only onto one, and that case is settled by
-// comparing with the binary64 value.
-__device__ __forceinline__ uint32_t bf16_bits_from_f64(double d) {
-    const float f = (float)d;
-    const uint32_t u = __float_as_uint(f);
-    if (__builtin_expect((u & 0xFFFFu) == 0x8000u, 0)) {
-        const double back = (double)f;
-        if (d != back) return (u >> 16) + (__builtin_fabs(d) > __builtin_fabs(back) ? 1u : 0u);
+// bf16 (round to nearest even) of 8 binary64 values, two per word, via fp32:
+// RN32 cannot move a value across a bf16 midpoint, only onto one, and that
+// rare case is settled by comparing with the binary64 value (one wave-uniform
+// branch, almost never taken).
+__device__ __forceinline__ void pack8_from_f64(const double (&d)[8], uint32_t (&w)[4]) {
+    float f[8];
+    bool tie = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[i] = (float)d[i];
+        tie |= (__float_as_uint(f[i]) & 0xFFFFu) == 0x8000u;
     }
-    return pack_bf16(f, f) & 0xFFFFu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack_bf16(f[2 * j], f[2 * j + 1]);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tie) != 0, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t u = __float_as_uint(f[i]);
+            if ((u & 0xFFFFu) != 0x8000u) continue;
+            const double back = (double)f[i];
+            if (d[i] == back) continue;
+            const uint32_t h = (u >> 16) + (__builtin_fabs(d[i]) > __builtin_fabs(back) ? 1u : 0u);
+            const int sh = (i & 1) * 16;
+            w[i / 2] = (w[i / 2] & ~(0xFFFFu << sh)) | (h << sh);
+        }
+    }
 }
 
 // ---- FP8 E4M3FN ------------------------------------------------------------
@@ -116,6 +165,23 @@ __device__ __forceinline__ uint32_t pack_e2m1x8(const float (&t)[8]) {
     return w;
 }
 
+// ---- reciprocal square root -------------------------------------------------
+
+// RN32(1 / sqrt(v)) for v > 0 within the fp32 range: fp32 reciprocal-sqrt seed,
+// two Newton steps in binary64 (error a few binary64 ulps), one rounding to
+// fp32. It differs from the correctly rounded value only when 1/sqrt(v) lies
+// within a few binary64 ulps of an fp32 rounding boundary.
+__device__ __forceinline__ float rsqrt_rn32(double v) {
+    double y = (double)__builtin_amdgcn_rsqf((float)v);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const double t = v * y;
+        const double e = __builtin_fma(-t, y, 1.0);  // 1 - v y^2
+        y = __builtin_fma(0.5 * y, e, y);
+    }
+    return (float)y;
+}
+
 // ---- wave64 reductions --------------------------------------------------------
 
 // DPP move of a 64-bit value (both halves with the same lane pattern).
@@ -144,6 +210,28 @@ __device__ __forceinline__ double wave_sum(double v) {
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
     return v;
+}
+
+// Sums of two binary64 values per thread over the whole workgroup (blockDim.x
+// a multiple of 64, at most 1024). Every thread receives the same bits: waves
+// reduce with wave_sum, then each thread adds the per-wave partials in wave
+// order. `scratch` holds 32 doubles of LDS; the call contains __syncthreads.
+__device__ __forceinline__ void block_sum2(double& a, double& b, double* scratch) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        scratch[wave] = a;
+        scratch[16 + wave] = b;
+    }
+    __syncthreads();
+    const int nwaves = blockDim.x >> 6;
+    a = 0.0;
+    b = 0.0;
+    for (int w = 0; w < nwaves; ++w) {
+        a += scratch[w];
+        b += scratch[16 + w];
+    }
 }
 
 }  // namespace dit

@@ -22,10 +22,10 @@ struct NormModulateArgs {
     const uint16_t* shift;   // [hidden]
     const float* input_scale;  // device scalar
     int64_t rows;
-    int32_t hidden;          // multiple of 8, <= kMaxHidden
+    int32_t hidden;          // multiple of 8, <= kMaxHidden (one thread per 8 columns)
     float eps;
 };
-constexpr int kMaxHidden = 6144;
+constexpr int kMaxHidden = 8192;
 hipError_t launch_norm_modulate_fp8(const NormModulateArgs& a, hipStream_t stream);
 
 struct QkvArgs {
@@ -45,6 +45,7 @@ struct QkvArgs {
 };
 constexpr int kHeadDim = 128;
 constexpr int kMaxHeads = 64;
+constexpr int kQkvHeadsPerWave = 24;  // heads handled by one wave of the QKV kernel
 hipError_t launch_qkv_epilogue(const QkvArgs& a, hipStream_t stream);
 
 struct BiasMulAddArgs {

@@ -8,12 +8,17 @@
 // ("Implementation breakdown" item 3: x + bias folded into the gated-residual
 // norm kernel).
 //
-// Layout on gfx950: one wave64 per row. A row of `hidden` bf16 is cut into
-// 16-byte chunks; lane l holds chunks l, l + 64, l + 128, ... (V of them), so
-// each load or store instruction of the wave moves 1 KiB of contiguous HBM.
-// The whole row stays in registers between the statistics and the outputs.
-// Row statistics are accumulated in binary64 and reduced with DPP within
-// 16-lane rows, then across rows.
+// Layout on gfx950: a row of `hidden` bf16 is cut into 16-byte chunks (8
+// values) and owned by WPR waves; wave w of the row takes chunks
+// 64 (w + WPR k) + lane for k < V, so each load or store instruction of a wave
+// moves 1 KiB of contiguous HBM. A workgroup holds RPW rows; it first issues
+// its streaming loads, then (when they fit in 48 KiB, kLds) converts the
+// row-broadcast vectors once into fp32 in LDS (1 + scale, shift, and gate,
+// bias for the residual variants), which takes those conversions off the
+// per-element path; otherwise each wave reads them from L2. The row stays in
+// registers between the statistics and the outputs. Statistics are binary64:
+// DPP/shuffle within each wave, then (WPR > 1) the wave partials through LDS,
+// added in wave order so every thread of the row agrees bit for bit.
 #include "dit_device.h"
 #include "kernels.h"
 
@@ -22,97 +27,168 @@ namespace {
 
 enum Mode : int { kPlain = 0, kResidual = 1, kBiasResidual = 2 };
 
-template <int V, int MODE>
-__global__ __launch_bounds__(256) void norm_modulate_fp8_kernel(NormModulateArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.rows) return;
-    const int cpr = a.hidden >> 3;  // 16-byte chunks per row
-    const int64_t base = row * (int64_t)a.hidden;
+// Number of fp32 column vectors staged in LDS per mode.
+template <int MODE>
+constexpr int kColVecs = MODE == kPlain ? 2 : (MODE == kResidual ? 3 : 4);
 
-    // Chunk k of this lane is column chunk c = lane + 64 k. Only the last one
-    // can fall beyond the row (V = ceil(cpr / 64)).
-    u32x4 xin[V];
-    u32x4 rin[V];
+__device__ __forceinline__ void lds_read8(const float* p, float (&f)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+__device__ __forceinline__ void lds_write8(float* p, const float (&f)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+constexpr size_t kLdsColsMax = 48 * 1024;  // bytes of fp32 column vectors staged in LDS
+
+// The 8 fp32 column values of chunk c of column vector `which` (0: 1 + scale,
+// 1: shift, 2: gate, 3: bias), from LDS or from the bf16 vector in memory.
+template <bool kLds>
+__device__ __forceinline__ void col8(const float* cols, const NormModulateArgs& a, int which,
+                                     int c, float (&f)[8]) {
+    if (kLds) {
+        lds_read8(cols + (size_t)which * a.hidden + 8 * c, f);
+        return;
+    }
+    const uint16_t* src = which == 0 ? a.scale : which == 1 ? a.shift : which == 2 ? a.gate : a.bias;
+    unpack8(load16(src + 8 * c), f);
+    if (which == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = 1.0f + f[i];
+    }
+}
+
+template <int MODE, int WPR, int RPW, int V, bool kLds>
+__global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormModulateArgs a,
+                                                                            double inv_hidden) {
+    // cols: [kColVecs][hidden] fp32 = 1 + scale, shift, gate, bias
+    extern __shared__ float cols[];
+    __shared__ double scratch[RPW][WPR][2];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rw = wave / WPR;  // row slot in the workgroup
+    const int sw = wave % WPR;  // wave within the row
+    const int64_t row = (int64_t)blockIdx.x * RPW + rw;
+    const bool active = row < a.rows;  // every wave still reaches the barriers
+    const int H = a.hidden;
+    const int cpr = H >> 3;  // chunks per row
+    const int64_t base = row * H;
+
+    // 1. Streaming loads of this wave's chunks.
+    u32x4 xin[V], rin[V];
+    bool ok[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        const int c = lane + 64 * k;
-        const bool ok = (k < V - 1) || (c < cpr);
-        xin[k] = ok ? load16(a.x + base + 8 * c) : (u32x4){0, 0, 0, 0};
-        if (MODE != kPlain) rin[k] = ok ? load16(a.residual + base + 8 * c) : (u32x4){0, 0, 0, 0};
+        const int c = 64 * (sw + WPR * k) + lane;
+        ok[k] = active && c < cpr;
+        xin[k] = ok[k] ? stream_load16(a.x + base + 8 * c) : (u32x4){0, 0, 0, 0};
+        if (MODE != kPlain) rin[k] = ok[k] ? stream_load16(a.residual + base + 8 * c) : (u32x4){0, 0, 0, 0};
     }
 
-    // v: the row to normalise (x, or the new residual).
+    // 2. Column vectors to fp32 in LDS, while the streaming loads are in flight.
+    if (kLds) {
+        for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
+#pragma unroll
+            for (int which = 0; which < kColVecs<MODE>; ++which) {
+                float f[8];
+                col8<false>(cols, a, which, c, f);
+                lds_write8(cols + (size_t)which * H + 8 * c, f);
+            }
+        }
+        __syncthreads();
+    }
+
+    // 3. The row to normalise: x, or the new residual (0 outside the row).
     float v[V][8];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        const int c = lane + 64 * k;
-        const bool ok = (k < V - 1) || (c < cpr);
+        const int c = 64 * (sw + WPR * k) + lane;
         if (MODE == kPlain) {
             unpack8(xin[k], v[k]);
-        } else {
-            float xf[8], rf[8], gf[8];
-            unpack8(xin[k], xf);
-            unpack8(rin[k], rf);
-            unpack8(ok ? load16(a.gate + 8 * c) : (u32x4){0, 0, 0, 0}, gf);
-            if (MODE == kBiasResidual) {
-                float bf[8];
-                unpack8(ok ? load16(a.bias + 8 * c) : (u32x4){0, 0, 0, 0}, bf);
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {  // xb = bf16(x + bias)
-                    const uint32_t w = pack_bf16(xf[i] + bf[i], xf[i + 1] + bf[i + 1]);
-                    xf[i] = bf_lo(w);
-                    xf[i + 1] = bf_hi(w);
-                }
-            }
-            uint32_t rw[4];
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                // gate * xb is exact in fp32 (8 x 8 significant bits); the sum
-                // with the residual is rounded once to bf16.
-                const uint32_t lo = bf16_bits_exact_sum(gf[i] * xf[i], rf[i]);
-                const uint32_t hi = bf16_bits_exact_sum(gf[i + 1] * xf[i + 1], rf[i + 1]);
-                rw[i / 2] = lo | (hi << 16);
-                v[k][i] = bf_lo(lo);
-                v[k][i + 1] = bf_lo(hi);
-            }
-            if (ok) store16(a.r_out + base + 8 * c, (u32x4){rw[0], rw[1], rw[2], rw[3]});
+            continue;
         }
+        float xf[8], rf[8], gf[8];
+        unpack8(xin[k], xf);
+        unpack8(rin[k], rf);
+        if (ok[k]) col8<kLds>(cols, a, 2, c, gf);
+        else for (int i = 0; i < 8; ++i) gf[i] = 0.0f;
+        if (MODE == kBiasResidual && ok[k]) {
+            float bf[8];
+            col8<kLds>(cols, a, 3, c, bf);
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {  // xb = bf16(x + bias)
+                const uint32_t w = pack_bf16(xf[i] + bf[i], xf[i + 1] + bf[i + 1]);
+                xf[i] = bf_lo(w);
+                xf[i + 1] = bf_hi(w);
+            }
+        }
+        // gate * xb is exact in fp32 (8 x 8 significant bits); the sum with the
+        // residual is rounded once to bf16.
+        float prod[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) prod[i] = gf[i] * xf[i];
+        uint32_t rw4[4];
+        pack8_exact_sum(prod, rf, rw4);
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            v[k][i] = bf_lo(rw4[i / 2]);
+            v[k][i + 1] = bf_hi(rw4[i / 2]);
+        }
+        if (ok[k]) store16(a.r_out + base + 8 * c, (u32x4){rw4[0], rw4[1], rw4[2], rw4[3]});
     }
 
-    // Mean and biased variance from one pass of binary64 sums. The square of
-    // a bf16 value is exact, so both sums are exact for ordinary rows and
+    // 4. Mean and biased variance from binary64 sums of v and v^2. The square
+    // of a bf16 value is exact, so both sums are exact for ordinary rows and
     // var = E[v^2] - mean^2 is within a few binary64 ulps of the two-pass
     // value unless |mean| dwarfs the spread by many orders of magnitude.
     double s1 = 0.0, s2 = 0.0;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        const bool ok = (k < V - 1) || (lane + 64 * k < cpr);
-        if (ok) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const double d = (double)v[k][i];
-                s1 += d;
-                s2 = __builtin_fma(d, d, s2);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const double d = (double)v[k][i];
+            s1 += d;
+            s2 = __builtin_fma(d, d, s2);
         }
     }
     s1 = wave_sum(s1);
     s2 = wave_sum(s2);
-    const double mean = s1 / (double)a.hidden;
-    const double var = __builtin_fmax(s2 / (double)a.hidden - mean * mean, 0.0);
-    const float factor = (float)(1.0 / __builtin_sqrt(var + (double)a.eps));
+    if (WPR > 1) {
+        if (lane == 0) {
+            scratch[rw][sw][0] = s1;
+            scratch[rw][sw][1] = s2;
+        }
+        __syncthreads();
+        s1 = 0.0;
+        s2 = 0.0;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) {
+            s1 += scratch[rw][w][0];
+            s2 += scratch[rw][w][1];
+        }
+    }
+    if (!active) return;
+    // mean = s1 / hidden within an ulp of binary64 (reciprocal from the host),
+    // factor = 1 / sqrt(var + eps) by binary64 Newton steps; both then rounded
+    // once to fp32.
+    const double mean = s1 * inv_hidden;
+    const double var = __builtin_fmax(s2 * inv_hidden - mean * mean, 0.0);
+    const float factor = rsqrt_rn32(var + (double)a.eps);
     const float mean32 = (float)mean;
     const float inv = 1.0f / *a.input_scale;  // IEEE division
 
+    // 5. Modulate, quantise, store.
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        const int c = lane + 64 * k;
-        const bool ok = (k < V - 1) || (c < cpr);
-        if (!ok) continue;
-        float sc[8], sh[8];
-        unpack8(load16(a.scale + 8 * c), sc);
-        unpack8(load16(a.shift + 8 * c), sh);
+        if (!ok[k]) continue;
+        const int c = 64 * (sw + WPR * k) + lane;
+        float ops[8], sh[8];
+        col8<kLds>(cols, a, 0, c, ops);
+        col8<kLds>(cols, a, 1, c, sh);
         uint32_t yw[4];
         float yv[8];
 #pragma unroll
@@ -120,8 +196,8 @@ __global__ __launch_bounds__(256) void norm_modulate_fp8_kernel(NormModulateArgs
             const float t0 = (v[k][i] - mean32) * factor;
             const float t1 = (v[k][i + 1] - mean32) * factor;
             const uint32_t nw = pack_bf16(t0, t1);  // normalised row, bf16
-            const float m0 = __builtin_fmaf(bf_lo(nw), 1.0f + sc[i], sh[i]);
-            const float m1 = __builtin_fmaf(bf_hi(nw), 1.0f + sc[i + 1], sh[i + 1]);
+            const float m0 = __builtin_fmaf(bf_lo(nw), ops[i], sh[i]);
+            const float m1 = __builtin_fmaf(bf_hi(nw), ops[i + 1], sh[i + 1]);
             yw[i / 2] = pack_bf16(m0, m1);
             yv[i] = bf_lo(yw[i / 2]);
             yv[i + 1] = bf_hi(yw[i / 2]);
@@ -135,24 +211,56 @@ __global__ __launch_bounds__(256) void norm_modulate_fp8_kernel(NormModulateArgs
     }
 }
 
+// Launch with WPR waves per row, RPW rows per workgroup and V chunks per lane
+// (V * 64 * WPR >= hidden / 8); kLds stages the column vectors in LDS.
+template <int MODE, int WPR, int RPW, int V, bool kLds>
+hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.rows + RPW - 1) / RPW));
+    const size_t lds = kLds ? (size_t)kColVecs<MODE> * a.hidden * sizeof(float) : 0;
+    hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds>), grid,
+                       dim3(64 * WPR * RPW), lds, stream, a, 1.0 / (double)a.hidden);
+    return hipGetLastError();
+}
+
+// Geometries measured on MI355X at hidden 3072 (time per call over
+// back-to-back launches with rotating buffers):
+//  - fewer than 1024 rows (latency-bound): six waves per row, two rows per
+//    workgroup, column vectors read from L2;
+//  - plain variant, many rows: two waves per row, four rows per workgroup;
+//  - residual variants, many rows: one wave per row, eight rows per workgroup,
+//    column vectors staged in LDS when they fit in 48 KiB.
 template <int MODE>
 hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
     const int cpr = a.hidden / 8;
-    const int V = (cpr + 63) / 64;
-    const dim3 grid((unsigned)((a.rows + 3) / 4));
-    const dim3 block(256);
-#define DIT_NM_CASE(VV)                                                              \
-    case VV:                                                                         \
-        hipLaunchKernelGGL((norm_modulate_fp8_kernel<VV, MODE>), grid, block, 0, stream, a); \
-        break;
-    switch (V) {
-        DIT_NM_CASE(1) DIT_NM_CASE(2) DIT_NM_CASE(3) DIT_NM_CASE(4)
-        DIT_NM_CASE(5) DIT_NM_CASE(6) DIT_NM_CASE(7) DIT_NM_CASE(8)
-        DIT_NM_CASE(9) DIT_NM_CASE(10) DIT_NM_CASE(11) DIT_NM_CASE(12)
-        default: return hipErrorInvalidValue;
+    if (a.rows < 1024) {
+        switch ((cpr + 383) / 384) {
+            case 1: return launch_geom<MODE, 6, 2, 1, false>(a, stream);
+            case 2: return launch_geom<MODE, 6, 2, 2, false>(a, stream);
+            default: return launch_geom<MODE, 6, 2, 3, false>(a, stream);  // up to 1152 chunks
+        }
     }
-#undef DIT_NM_CASE
-    return hipGetLastError();
+    if constexpr (MODE != kPlain) {
+        if (cpr > 384) goto two_waves;
+        const bool lds = (size_t)kColVecs<MODE> * a.hidden * sizeof(float) <= kLdsColsMax;
+        switch ((cpr + 63) / 64) {
+#define DIT_NM_ONE_WAVE(VV)                                                                    \
+    case VV:                                                                                   \
+        return lds ? launch_geom<MODE, 1, 8, VV, true>(a, stream)                             \
+                   : launch_geom<MODE, 1, 8, VV, false>(a, stream);
+            DIT_NM_ONE_WAVE(1) DIT_NM_ONE_WAVE(2) DIT_NM_ONE_WAVE(3)
+            DIT_NM_ONE_WAVE(4) DIT_NM_ONE_WAVE(5) DIT_NM_ONE_WAVE(6)
+#undef DIT_NM_ONE_WAVE
+        }
+    }
+two_waves:
+    switch ((cpr + 127) / 128) {
+        case 1: return launch_geom<MODE, 2, 4, 1, false>(a, stream);
+        case 2: return launch_geom<MODE, 2, 4, 2, false>(a, stream);
+        case 3: return launch_geom<MODE, 2, 4, 3, false>(a, stream);
+        case 4: return launch_geom<MODE, 2, 4, 4, false>(a, stream);
+        case 5: case 6: return launch_geom<MODE, 2, 4, 6, false>(a, stream);
+        default: return launch_geom<MODE, 2, 4, 8, false>(a, stream);  // up to 1024 chunks
+    }
 }
 
 }  // namespace

@@ -8,12 +8,12 @@
 // epsilon, rotated by interleaved (non-NeoX) RoPE from an fp32 cache, V is
 // copied, and all three are written in [text, image] order.
 //
-// Layout on gfx950: one wave64 per (joint token, part in {Q, K, V}, block of up
-// to 24 heads). The wave is four 16-lane rows; row r takes heads r, r+4, ...,
-// r+20 of the block, and lane s of a row holds elements 8s..8s+7 of its head
-// (one 16-byte load). A head's sum of squares is a 16-lane DPP reduction, the
-// RoPE pairs (2i, 2i+1) sit inside one lane, and the lane's four cos/sin
-// values are loaded once and reused for all its heads.
+// Layout on gfx950: one wave64 per (joint token, part in {Q, K, V}, group of
+// kPasses * 4 heads). The wave is four 16-lane rows; row r takes heads r,
+// r + 4, ... of its group, and lane s of a row holds elements 8s..8s+7 of its
+// head (one 16-byte load). A head's sum of squares is a 16-lane DPP
+// reduction, the RoPE pairs (2i, 2i+1) sit inside one lane, and the lane's
+// four cos/sin values are loaded once per wave.
 //
 // Rounding: the RMS statistic is binary64; 1/sqrt is refined in binary64 from
 // the fp32 seed and rounded once to fp32; the normalised head is rounded to
@@ -25,23 +25,11 @@
 namespace dit {
 namespace {
 
-constexpr int kHeadsPerWave = 24;  // 6 passes of 4 heads
-
-// RN32(1 / sqrt(v)) for v > 0 in the fp32 range: fp32 reciprocal-sqrt seed,
-// two Newton steps in binary64, one rounding to fp32.
-__device__ __forceinline__ float rsqrt_rn32(double v) {
-    double y = (double)__builtin_amdgcn_rsqf((float)v);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const double t = v * y;
-        const double e = __builtin_fma(-t, y, 1.0);  // 1 - v y^2
-        y = __builtin_fma(0.5 * y, e, y);
-    }
-    return (float)y;
-}
-
+// kPasses 4-head passes per wave (a wave covers 4 * kPasses heads).
+template <int kPasses>
 __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t units_per_part,
                                                            uint32_t hblocks) {
+    constexpr int kHeadsPerWave = 4 * kPasses;
     const int lane = threadIdx.x & 63;
     const int r = lane >> 4;  // head slot within a pass
     const int s = lane & 15;  // 8-element slice of the head
@@ -57,18 +45,18 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
                           i * (is_txt ? a.txt_stride : a.img_stride);
     uint16_t* dst = a.joint[part] + j * (int64_t)a.heads * kHeadDim;
 
-    int head[6];
-    u32x4 xin[6];
+    int head[kPasses];
+    u32x4 xin[kPasses];
 #pragma unroll
-    for (int p = 0; p < 6; ++p) {
+    for (int p = 0; p < kPasses; ++p) {
         head[p] = (int)hb * kHeadsPerWave + 4 * p + r;
-        xin[p] = head[p] < a.heads ? load16(src + head[p] * kHeadDim + 8 * s)
+        xin[p] = head[p] < a.heads ? stream_load16(src + head[p] * kHeadDim + 8 * s)
                                    : (u32x4){0, 0, 0, 0};
     }
 
     if (part == 2) {  // V: bit copy into the joint layout
 #pragma unroll
-        for (int p = 0; p < 6; ++p)
+        for (int p = 0; p < kPasses; ++p)
             if (head[p] < a.heads) store16(dst + head[p] * kHeadDim + 8 * s, xin[p]);
         return;
     }
@@ -84,7 +72,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
     const double eps = (double)(is_txt ? a.txt_eps : a.img_eps);
 
 #pragma unroll
-    for (int p = 0; p < 6; ++p) {
+    for (int p = 0; p < kPasses; ++p) {
         // Inactive head slots compute on zeros (all 16 lanes of a row agree,
         // so the row reduction never mixes live and dead lanes) and skip the
         // store.
@@ -92,7 +80,10 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
         unpack8(xin[p], x);
         double ss = 0.0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += (double)(x[e] * x[e]);  // bf16 squares are exact
+        for (int e = 0; e < 8; ++e) {
+            const double d = (double)x[e];
+            ss = __builtin_fma(d, d, ss);  // bf16 squares are exact
+        }
         ss = row16_sum(ss);
         const float inv = rsqrt_rn32(ss * (1.0 / kHeadDim) + eps);
 
@@ -103,29 +94,36 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
             n[e] = bf_lo(nw);
             n[e + 1] = bf_hi(nw);
         }
-        uint32_t ow[4];
+        double o[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const double n0 = (double)n[2 * q];
             const double n1 = (double)n[2 * q + 1];
             // bf16 x fp32 products are exact in binary64: one rounding each.
-            const double o0 = __builtin_fma(n0, cs[q], -(n1 * sn[q]));
-            const double o1 = __builtin_fma(n1, cs[q], n0 * sn[q]);
-            ow[q] = bf16_bits_from_f64(o0) | (bf16_bits_from_f64(o1) << 16);
+            o[2 * q] = __builtin_fma(n0, cs[q], -(n1 * sn[q]));
+            o[2 * q + 1] = __builtin_fma(n1, cs[q], n0 * sn[q]);
         }
+        uint32_t ow[4];
+        pack8_from_f64(o, ow);
         if (head[p] < a.heads)
             store16(dst + head[p] * kHeadDim + 8 * s, (u32x4){ow[0], ow[1], ow[2], ow[3]});
     }
 }
 
-}  // namespace
-
-hipError_t launch_qkv_epilogue(const QkvArgs& a, hipStream_t stream) {
-    const uint32_t hblocks = (uint32_t)((a.heads + kHeadsPerWave - 1) / kHeadsPerWave);
+template <int kPasses>
+hipError_t launch_passes(const QkvArgs& a, hipStream_t stream) {
+    const uint32_t hblocks = (uint32_t)((a.heads + 4 * kPasses - 1) / (4 * kPasses));
     const uint32_t units = (uint32_t)((a.txt_rows + a.img_rows) * hblocks);
     const dim3 grid((units + 3) / 4, 3);
-    hipLaunchKernelGGL(qkv_epilogue_kernel, grid, dim3(256), 0, stream, a, units, hblocks);
+    hipLaunchKernelGGL(qkv_epilogue_kernel<kPasses>, grid, dim3(256), 0, stream, a, units, hblocks);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// Six passes (24 heads per wave) measured best on MI355X at 24 heads x 128.
+hipError_t launch_qkv_epilogue(const QkvArgs& a, hipStream_t stream) {
+    return launch_passes<kQkvHeadsPerWave / 4>(a, stream);
 }
 
 }  // namespace dit

@@ -75,7 +75,7 @@ def test_norm_modulate_refusals(native):
     assert _nm(L, rows=-1) == native.DIT_ERR_SHAPE
     assert _nm(L, hidden=0) == native.DIT_ERR_SHAPE
     assert _nm(L, hidden=3076) == native.DIT_ERR_UNSUPPORTED
-    assert _nm(L, hidden=6152) == native.DIT_ERR_UNSUPPORTED
+    assert _nm(L, hidden=8200) == native.DIT_ERR_UNSUPPORTED
     assert _nm(L, x=FAKE + 2) == native.DIT_ERR_ALIGN
     assert _nm(L, q=FAKE + 8) == native.DIT_ERR_ALIGN
     assert _nm(L, s=FAKE + 2) == native.DIT_ERR_ALIGN

@@ -82,8 +82,9 @@ NORM_CASES = [
     (1024, 3072, 0.02, 2),
     (4096, 3072, 0.5, 3),     # full image-token count
     (33, 512, 0.0625, 4),
-    (17, 1000, 0.0625, 5),    # ragged: 125 chunks over 64 lanes
-    (9, 6144, 0.02, 6),       # FLUX.2 width, 12 chunks per lane
+    (17, 1000, 0.0625, 5),    # ragged: 125 chunks, a partial last wave
+    (9, 6144, 0.02, 6),       # FLUX.2 width, 12 waves per row
+    (3, 8192, 0.0625, 8),     # widest supported row: 1024 threads
     (5, 8, 0.0625, 7),        # one chunk per row
 ]
 
@@ -223,7 +224,7 @@ BMA_CASES = [
     (3, 1000, True, 2),
     (5, 6144, True, 3),
     (1, 8, True, 4),
-    (2, 25600, True, 5),     # a row longer than one unrolled step
+    (2, 25600, True, 5),     # a row longer than one 1024-thread pass
 ]
 
 
