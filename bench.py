@@ -176,34 +176,81 @@ class Workload:
 
 
 def time_steps(torch, wl, steps, per_kernel):
-    """Outer-event timing of `steps` steps; with per_kernel, an event pair
-    around every launch (on torch's current stream, where the kernels run)."""
+    """Outer-event timing of `steps` steps. With per_kernel, one more event is
+    recorded after every launch (on torch's current stream, where the kernels
+    run): launch i lasts from the event before it to the event after it. All
+    events are created before the timed region, so the host only launches and
+    records inside it and stays ahead of the GPU."""
     stream = torch.cuda.current_stream()
     names = [n for n, _, _ in wl.launches]
-    pairs = {n: [] for n in names}
+    n_marks = steps * (len(names) + 1) if per_kernel else 0
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_marks)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    labels = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
+    m = 0
     for _ in range(steps):
+        if per_kernel:
+            events[m].record(stream)
+            labels.append(None)
+            m += 1
         for n, _, fn in wl.launches:
+            fn()
             if per_kernel:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                pairs[n].append((e0, e1))
-            else:
-                fn()
+                events[m].record(stream)
+                labels.append(n)
+                m += 1
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    kern = {n: sorted(e0.elapsed_time(e1) for e0, e1 in pairs[n]) for n in names} if per_kernel else {}
-    return total_ms, wall, kern
+    kern = {n: [] for n in names}
+    for i in range(1, m):
+        if labels[i] is not None:
+            kern[labels[i]].append(events[i - 1].elapsed_time(events[i]))
+    return total_ms, wall, {n: sorted(t) for n, t in kern.items()}
 
 
-def cpu_baseline(sample_div=3):
+# Source files that define each launch's kernel (for matching profiled traffic).
+KERNEL_SOURCES = {
+    "norm_img": "norm_modulate.hip", "norm_txt": "norm_modulate.hip", "sr_norm": "norm_modulate.hip",
+    "qkv": "qkv_epilogue.hip", "bma": "bias_mul_add.hip", "cat_fp8": "token_cat_quant.hip",
+    "cat_fp4": "token_cat_quant.hip",
+}
+
+
+def kernel_source_hash(name):
+    """sha256 over the kernel's source file and the shared device headers."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "quant_epilogues_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[name], "dit_device.h", "kernels.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a plain-copy calibration), from the committed summary in
+    profiles/; None if absent or if the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_qwen_flux_step.md")
+    try:
+        with open(path) as f:
+            text = f.read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)["launches"][name]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash(name):
+        return None
+    return rec["hbm_bytes"]
+
+
+def cpu_baseline(sample_div=2):
     """The CPU oracle, single-threaded, on a row sample of the same step."""
     import numpy as np
 
@@ -285,14 +332,19 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-sample-div", type=int, default=3,
+    ap.add_argument("--cpu-sample-div", type=int, default=2,
                     help="the CPU oracle runs on 1/N of each epilogue's rows")
     ap.add_argument("--only", default="", help="comma-separated subset of launches to time")
+    ap.add_argument("--print-source-hashes", action="store_true",
+                    help="print the source hash of every launch's kernel and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--blocks", type=int, default=0,
                     help="also time a Qwen-Image block sequence of this many blocks (e.g. 60)")
     args = ap.parse_args()
+    if args.print_source_hashes:
+        print(json.dumps({n: kernel_source_hash(n) for n in KERNEL_SOURCES}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: these epilogues need no cross-GPU exchange and "
               "this build runs on a single MI355X; run with --gpus 1", file=sys.stderr)
@@ -325,6 +377,7 @@ def main():
                          "pct_peak": round(100 * nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
     dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
     achieved = kernels[dom]["gb_s"]
+    traffic = profiled_traffic(dom)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -339,7 +392,8 @@ def main():
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": kernels[dom]["bytes"]},
     }
     if args.blocks:
         out["block_sequence"] = block_sequence(torch, qe, args.blocks, reps=3)
