@@ -25,6 +25,8 @@
  *     where the split path materialises a tensor.
  *
  * Readings taken where the pages are silent are listed beside each function.
+ * Parity unpinned: the FP4 group arithmetic of oracle_token_cat_fp4 against the
+ * third-party primitive the sglang PR 37141 page delegates it to (see there).
  */
 #include "oracle.h"
 
@@ -423,7 +425,10 @@ void oracle_token_cat_fp8(uint8_t* out, float* pre, const uint16_t* a,
  *   s_pre = RN32(RN32(amax / 6) * g); s8 = e4m3(min(s_pre, 448));
  *   k = RN32(g / dec(s8)) (zero scale -> every code +0);
  *   code = e2m1(RN32(x * k)); byte j = code(2j) | code(2j+1) << 4.
- * Scales are row-major [round_up(rows, 128), cols / 16]. */
+ * Scales are row-major [round_up(rows, 128), cols / 16].
+ * Pinned by closed forms (exactly representable groups, zero and saturating
+ * groups, the dequantisation error bound); parity with the page's third-party
+ * primitive itself is unpinned, since the page shows none of its outputs. */
 void oracle_token_cat_fp4(uint8_t* packed, uint8_t* scales, float* s_pre,
                           float* pre, const uint16_t* a, int64_t a_cols,
                           const uint16_t* b, int64_t b_cols, int64_t rows,
