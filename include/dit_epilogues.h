@@ -24,7 +24,8 @@
  *  - Validation is host-only and happens before any HIP call: NULL pointers
  *    (DIT_ERR_NULL), negative or inconsistent sizes (DIT_ERR_SHAPE), pointers
  *    not 16-byte aligned (DIT_ERR_ALIGN), shapes outside the instantiated
- *    kernels (DIT_ERR_UNSUPPORTED). A failing launch returns DIT_ERR_HIP.
+ *    kernels or too large for one launch, whose grid may cover at most 2^32
+ *    lanes (DIT_ERR_UNSUPPORTED). A failing launch returns DIT_ERR_HIP.
  *
  * Sources: the five sglang pull-request summary pages on prhub.com.cn that
  * describe these fusions (PRs 37123, 37156, 37162, 37116, 37141). Each entry

@@ -39,11 +39,15 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 int launched(hipError_t e, const char* what) {
+    if (e == dit::kGridTooLarge)
+        return fail(DIT_ERR_UNSUPPORTED, "%s: too large for one launch (grid limit of 2^32 lanes)", what);
     if (e != hipSuccess) return fail(DIT_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
 }
 
-constexpr int64_t kMaxRows = (int64_t(1) << 31) - 128;  // one workgroup row per grid.x index
+// Coarse bound that keeps row arithmetic (padding to 128 rows, products with
+// row widths) far from overflow; the launchers check the exact grid limit.
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 128;
 
 }  // namespace
 
@@ -162,7 +166,7 @@ int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v, const void* im
         return fail(DIT_ERR_SHAPE, "%s: row strides must be >= heads*head_dim (%lld) and a multiple of 8",
                     fn, (long long)width);
     const int64_t hblocks = (heads + dit::kQkvHeadsPerWave - 1) / dit::kQkvHeadsPerWave;
-    if ((img_rows + txt_rows) * hblocks >= (int64_t(1) << 32) - 4)
+    if (img_rows > kMaxRows || txt_rows > kMaxRows || (img_rows + txt_rows) * hblocks >= (int64_t(1) << 32) - 4)
         return fail(DIT_ERR_UNSUPPORTED, "%s: too many tokens", fn);
     const void* ptrs16[] = {joint_q, joint_k, joint_v};
     for (const void* p : ptrs16)
@@ -244,7 +248,7 @@ int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales, const v
     if (a_cols % 16 != 0 || b_cols % 16 != 0 || a_cols < 16)
         return fail(DIT_ERR_SHAPE, "%s: a_cols (%lld) and b_cols (%lld) must be multiples of 16, a_cols >= 16",
                     fn, (long long)a_cols, (long long)b_cols);
-    if (a_cols + b_cols > (int64_t(1) << 28) || rows > kMaxRows)  // grid.y = cols / 4096 tiles
+    if (a_cols + b_cols > (int64_t(1) << 28) || rows > kMaxRows)
         return fail(DIT_ERR_UNSUPPORTED, "%s: shape too large", fn);
     if (!out || !a || !scale_dev || (b_cols > 0 && !b) ||
         (kind == DIT_QUANT_FP4_E2M1 && !out_scales))

@@ -70,9 +70,10 @@ __global__ __launch_bounds__(64 * WPR * RPW) void bias_mul_add_kernel(BiasMulAdd
 
 template <bool kHasBias, int WPR, int RPW, int V>
 hipError_t launch_geom(const BiasMulAddArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.rows + RPW - 1) / RPW));
-    hipLaunchKernelGGL((bias_mul_add_kernel<kHasBias, WPR, RPW, V>), grid, dim3(64 * WPR * RPW), 0,
-                       stream, a);
+    const uint64_t blocks = (uint64_t)((a.rows + RPW - 1) / RPW);
+    if (blocks * (64 * WPR * RPW) >= kMaxGridLanes) return kGridTooLarge;
+    hipLaunchKernelGGL((bias_mul_add_kernel<kHasBias, WPR, RPW, V>), dim3((unsigned)blocks),
+                       dim3(64 * WPR * RPW), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -8,6 +8,11 @@
 
 namespace dit {
 
+// A launch covers at most 2^32 lanes along its grid's x dimension. Launchers
+// return kGridTooLarge, before calling HIP, for sizes that would need more.
+constexpr uint64_t kMaxGridLanes = uint64_t(1) << 32;
+constexpr hipError_t kGridTooLarge = hipErrorInvalidConfiguration;
+
 // LayerNorm + AdaLN modulation + static FP8 (optionally after bias + gated
 // residual). residual == nullptr selects the plain variant.
 struct NormModulateArgs {

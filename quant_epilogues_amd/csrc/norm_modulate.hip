@@ -215,9 +215,10 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
 // (V * 64 * WPR >= hidden / 8); kLds stages the column vectors in LDS.
 template <int MODE, int WPR, int RPW, int V, bool kLds>
 hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.rows + RPW - 1) / RPW));
+    const uint64_t blocks = (uint64_t)((a.rows + RPW - 1) / RPW);
+    if (blocks * (64 * WPR * RPW) >= kMaxGridLanes) return kGridTooLarge;
     const size_t lds = kLds ? (size_t)kColVecs<MODE> * a.hidden * sizeof(float) : 0;
-    hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds>), grid,
+    hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds>), dim3((unsigned)blocks),
                        dim3(64 * WPR * RPW), lds, stream, a, 1.0 / (double)a.hidden);
     return hipGetLastError();
 }

@@ -113,9 +113,11 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
 template <int kPasses>
 hipError_t launch_passes(const QkvArgs& a, hipStream_t stream) {
     const uint32_t hblocks = (uint32_t)((a.heads + 4 * kPasses - 1) / (4 * kPasses));
-    const uint32_t units = (uint32_t)((a.txt_rows + a.img_rows) * hblocks);
-    const dim3 grid((units + 3) / 4, 3);
-    hipLaunchKernelGGL(qkv_epilogue_kernel<kPasses>, grid, dim3(256), 0, stream, a, units, hblocks);
+    const uint64_t units = (uint64_t)(a.txt_rows + a.img_rows) * hblocks;
+    const uint64_t blocks = (units + 3) / 4;
+    if (blocks * 256 >= kMaxGridLanes) return kGridTooLarge;
+    hipLaunchKernelGGL(qkv_epilogue_kernel<kPasses>, dim3((unsigned)blocks, 3), dim3(256), 0, stream, a,
+                       (uint32_t)units, hblocks);
     return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@
 // are plain IEEE fp32 steps): s8 = e4m3(min((amax / 6) * g, 448)),
 // k = g / value(s8), code = e2m1(x * k); a zero scale gives zero codes.
 //
-// Layout on gfx950: a 2-D grid of (row, tile of chunks). FP8: each lane takes
+// Layout on gfx950: one workgroup per (row, tile of chunks), numbered in
+// address order. FP8: each lane takes
 // 8-element chunks (one 16-byte streaming load -> one 8-byte store), so every
 // load instruction of a wave reads 1 KiB contiguously. FP4: one lane per
 // 16-element group (two 16-byte loads -> 8 packed bytes + 1 scale byte; a
@@ -45,98 +46,58 @@ __device__ __forceinline__ void load16x2(const uint16_t* src, float (&f)[16]) {
     }
 }
 
-// U chunks per thread, kTile apart: a workgroup covers U * kTile chunks.
-// kElems = 16: a chunk is 16 elements (two 16-byte loads, one 16-byte store);
-// kElems = 8: a chunk is 8 elements (one 16-byte load, one 8-byte store), so
-// each load instruction of a wave reads 1 KiB contiguously.
-template <int U, int kElems>
-__global__ __launch_bounds__(kTile) void token_cat_fp8_kernel(TokenCatArgs a) {
-    const int64_t row = blockIdx.x;
+// Workgroups are numbered row-major over (row, tile): workgroup b covers tile
+// b % tiles of row b / tiles, so consecutive workgroups sweep memory in address
+// order. On MI355X this measured 5-10% faster than a (row, tile) grid whose
+// fastest index is the row.
+__device__ __forceinline__ void row_tile(uint32_t tiles, int64_t& row, int& tile) {
+    const uint32_t r = blockIdx.x / tiles;
+    row = r;
+    tile = (int)(blockIdx.x - r * tiles);
+}
+
+// FP8: U chunks of 8 elements per thread, kTile apart, so a workgroup covers
+// U * kTile chunks and each load instruction of a wave reads 1 KiB of one row
+// contiguously (one 16-byte streaming load -> one 8-byte store per chunk).
+template <int U>
+__global__ __launch_bounds__(kTile) void token_cat_fp8_kernel(TokenCatArgs a, uint32_t tiles) {
+    int64_t row;
+    int tile;
+    row_tile(tiles, row, tile);
     const int64_t cols = a.a_cols + a.b_cols;
-    const int cpr = (int)(cols / kElems);
-    const int a_chunks = (int)(a.a_cols / kElems);
+    const int cpr = (int)(cols >> 3);
+    const int a_chunks = (int)(a.a_cols >> 3);
     const float inv = 1.0f / *a.scale;  // IEEE division
-    float f[U][kElems];
+    float f[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int c = (blockIdx.y * U + u) * kTile + threadIdx.x;
+        const int c = (tile * U + u) * kTile + threadIdx.x;
         if (c >= cpr) continue;
-        const uint16_t* src = c < a_chunks ? a.a + row * a.a_cols + kElems * c
-                                           : a.b + row * a.b_cols + kElems * (c - a_chunks);
-#pragma unroll
-        for (int h = 0; h < kElems / 8; ++h) {
-            float t[8];
-            unpack8(stream_load16(src + 8 * h), t);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[u][8 * h + e] = t[e];
-        }
+        const uint16_t* src = c < a_chunks ? a.a + row * a.a_cols + 8 * c
+                                           : a.b + row * a.b_cols + 8 * (c - a_chunks);
+        unpack8(stream_load16(src), f[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int c = (blockIdx.y * U + u) * kTile + threadIdx.x;
+        const int c = (tile * U + u) * kTile + threadIdx.x;
         if (c >= cpr) continue;
-        uint32_t w[kElems / 4];
-#pragma unroll
-        for (int q = 0; q < kElems / 4; ++q)
-            w[q] = pack_e4m3x4(clamp_e4m3(f[u][4 * q] * inv), clamp_e4m3(f[u][4 * q + 1] * inv),
-                               clamp_e4m3(f[u][4 * q + 2] * inv), clamp_e4m3(f[u][4 * q + 3] * inv));
-        uint8_t* dst = a.out + row * cols + kElems * c;
-        if (kElems == 16) store16(dst, (u32x4){w[0], w[1], w[2], w[3]});
-        else store8(dst, (u32x2){w[0], w[1]});
+        const uint32_t w0 = pack_e4m3x4(clamp_e4m3(f[u][0] * inv), clamp_e4m3(f[u][1] * inv),
+                                        clamp_e4m3(f[u][2] * inv), clamp_e4m3(f[u][3] * inv));
+        const uint32_t w1 = pack_e4m3x4(clamp_e4m3(f[u][4] * inv), clamp_e4m3(f[u][5] * inv),
+                                        clamp_e4m3(f[u][6] * inv), clamp_e4m3(f[u][7] * inv));
+        store8(a.out + row * cols + 8 * c, (u32x2){w0, w1});
     }
 }
 
-// FP4 with two lanes per 16-element group: lane 2g + h holds elements 8h..8h+7
-// of group g (one 16-byte load; a wave reads 1 KiB contiguously); the group
-// maximum is exchanged between the two lanes with one DPP step, both lanes
-// derive the same scale, each writes 4 packed bytes, the even lane the scale.
-__global__ __launch_bounds__(kTile) void token_cat_fp4_pair_kernel(TokenCatArgs a) {
-    const int64_t row = blockIdx.x;  // < round_up(rows, 128)
+// FP4: one lane per 16-element group (two 16-byte loads -> 8 packed bytes and
+// one scale byte); rows past `rows` only write their zero scales.
+__global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a, uint32_t tiles) {
+    int64_t row;  // < round_up(rows, 128)
+    int tile;
+    row_tile(tiles, row, tile);
     const int64_t cols = a.a_cols + a.b_cols;
     const int groups = (int)(cols >> 4);
-    const int half = (int)(blockIdx.y * kTile + threadIdx.x);  // 8-element half-group
-    const int g = half >> 1;
-    const int h = half & 1;
-    const bool live = g < groups;  // whole pairs only: groups * 2 halves
-    if (row >= a.rows) {  // pad rows of the scale matrix
-        if (live && h == 0) a.out_scales[row * groups + g] = 0;
-        return;
-    }
-    const float gscale = *a.scale;  // global inverse scale
-    const int a_groups = (int)(a.a_cols >> 4);
-    float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (live) {
-        const uint16_t* src = g < a_groups ? a.a + row * a.a_cols + 16 * g + 8 * h
-                                           : a.b + row * a.b_cols + 16 * (g - a_groups) + 8 * h;
-        unpack8(stream_load16(src), f);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[e]));
-    const float other = __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false));
-    amax = __builtin_fmaxf(amax, other);  // lanes 2g and 2g + 1 exchange (quad_perm [1,0,3,2])
-    if (!live) return;
-    const float s_pre = (amax / 6.0f) * gscale;
-    const uint32_t s8 =
-        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s_pre, 448.0f), 0.0f, 0, false) & 0xFFu;
-    uint32_t packed = 0;
-    if (s8 != 0) {
-        const float kq = gscale / e4m3_value_pos(s8);  // IEEE division
-        float t[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = f[e] * kq;
-        packed = pack_e2m1x8(t);
-    }
-    store4(a.out + row * (cols >> 1) + 8 * g + 4 * h, packed);
-    if (h == 0) a.out_scales[row * groups + g] = (uint8_t)s8;
-}
-
-__global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a) {
-    const int64_t row = blockIdx.x;  // < round_up(rows, 128)
-    const int64_t cols = a.a_cols + a.b_cols;
-    const int groups = (int)(cols >> 4);
-    const int g = blockIdx.y * kTile + threadIdx.x;
+    const int g = tile * kTile + threadIdx.x;
     if (g >= groups) return;
     uint8_t* scale_out = a.out_scales + row * groups + g;
     if (row >= a.rows) {  // pad rows of the scale matrix
@@ -167,37 +128,34 @@ __global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a) {
     *scale_out = (uint8_t)s8;
 }
 
-template <int U, int kElems>
-hipError_t launch_fp8_u(const TokenCatArgs& a, hipStream_t stream) {
-    const int64_t chunks = (a.a_cols + a.b_cols) / kElems;
-    const dim3 grid((unsigned)a.rows, (unsigned)((chunks + U * kTile - 1) / (U * kTile)));
-    hipLaunchKernelGGL((token_cat_fp8_kernel<U, kElems>), grid, dim3(kTile), 0, stream, a);
+// One workgroup per (row, tile), numbered row-major; kGridTooLarge if the
+// launch would exceed the grid limit.
+template <typename Kernel>
+hipError_t launch_rows_tiles(Kernel kernel, const TokenCatArgs& a, int64_t rows, int64_t per_tile,
+                             int64_t units_per_row, hipStream_t stream) {
+    const uint64_t tiles = (uint64_t)((units_per_row + per_tile - 1) / per_tile);
+    const uint64_t blocks = (uint64_t)rows * tiles;
+    if (blocks * kTile >= kMaxGridLanes) return kGridTooLarge;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kTile), 0, stream, a, (uint32_t)tiles);
     return hipGetLastError();
 }
 
-hipError_t launch_fp4_pair(const TokenCatArgs& a, hipStream_t stream) {
-    const int64_t rows_padded = (a.rows + 127) / 128 * 128;
-    const int64_t halves = (a.a_cols + a.b_cols) / 8;
-    const dim3 grid((unsigned)rows_padded, (unsigned)((halves + kTile - 1) / kTile));
-    hipLaunchKernelGGL(token_cat_fp4_pair_kernel, grid, dim3(kTile), 0, stream, a);
-    return hipGetLastError();
-}
+constexpr int kFp8ChunksPerThread = 2;
 
 }  // namespace
 
-// 8 elements per lane, two chunks per thread: measured best on MI355X at
-// 4608 x (6144 + 18432) (~75% of HBM peak).
+// Two 8-element chunks per thread measured best on MI355X at
+// 4608 x (6144 + 18432).
 hipError_t launch_token_cat_fp8(const TokenCatArgs& a, hipStream_t stream) {
-    return launch_fp8_u<2, 8>(a, stream);
+    return launch_rows_tiles(token_cat_fp8_kernel<kFp8ChunksPerThread>, a, a.rows,
+                             (int64_t)kFp8ChunksPerThread * kTile, (a.a_cols + a.b_cols) / 8, stream);
 }
 
 // One lane per 16-element group measured faster than two lanes per group.
 hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream) {
     const int64_t rows_padded = (a.rows + 127) / 128 * 128;
-    const int64_t groups = (a.a_cols + a.b_cols) / 16;
-    const dim3 grid((unsigned)rows_padded, (unsigned)((groups + kTile - 1) / kTile));
-    hipLaunchKernelGGL(token_cat_fp4_kernel, grid, dim3(kTile), 0, stream, a);
-    return hipGetLastError();
+    return launch_rows_tiles(token_cat_fp4_kernel, a, rows_padded, kTile, (a.a_cols + a.b_cols) / 16,
+                             stream);
 }
 
 }  // namespace dit

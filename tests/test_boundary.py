@@ -157,3 +157,22 @@ def test_python_binding_has_no_cpu_path(native):
     x = torch.zeros(4, 3072, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qe.norm_modulate_fp8(x, x[0], x[0], torch.ones(1), 1e-6)
+
+
+def test_refuses_launches_beyond_the_grid_limit(native):
+    # Each launch covers at most 2^32 lanes; larger sizes are refused on the
+    # host with DIT_ERR_UNSUPPORTED instead of failing inside HIP.
+    L = native.lib()
+    big = 1 << 30
+    assert _nm(L, rows=big) == native.DIT_ERR_UNSUPPORTED
+    assert "grid limit" in native.last_error()
+    f = L.dit_scale_residual_norm_modulate_fp8
+    assert f(*([FAKE] * 10 + [big, 3072, 1e-6, None])) == native.DIT_ERR_UNSUPPORTED
+    assert _qkv(L, img_rows=1 << 27) == native.DIT_ERR_UNSUPPORTED
+    assert L.dit_bias_mul_add(FAKE, FAKE, None, FAKE, FAKE, big, 3072, None) == native.DIT_ERR_UNSUPPORTED
+    cat = L.dit_token_cat_quant
+    assert cat(native.DIT_QUANT_FP8_E4M3, FAKE, None, FAKE, 6144, FAKE2, 18432, big, FAKE,
+               None) == native.DIT_ERR_UNSUPPORTED
+    assert cat(native.DIT_QUANT_FP4_E2M1, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, big, FAKE,
+               None) == native.DIT_ERR_UNSUPPORTED
+    assert "grid limit" in native.last_error()

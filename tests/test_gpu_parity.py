@@ -274,6 +274,7 @@ FP8_CASES = [
     (7, 96, 160, 0.05, 1, False),
     (3, 6144, 0, 0.5, 2, False),
     (130, 16, 48, 0.4754464328, 3, False),
+    (5, 6144, 2064, 0.05, 7, False),         # 1026 chunks: three tiles, the last ragged
 ]
 
 
@@ -313,6 +314,7 @@ FP4_CASES = [
     (9, 32, 32, 1e4, 3, False),              # saturating scales
     (128, 6144, 0, "calibrated", 4, False),
     (129, 16, 16, "calibrated", 5, False),
+    (19, 4112, 4112, "calibrated", 6, False),  # 514 groups: three tiles, the last ragged
 ]
 
 
