@@ -9,13 +9,15 @@ One step = one pass over every fused epilogue at its full workload shape:
   cat_fp8    dit_token_cat_quant FP8               [4608, 6144 + 18432]
   cat_fp4    dit_token_cat_quant FP4               [4608, 6144 + 18432]
 Inputs are seeded synthetic tensors already resident in HBM; every launch has
-its own buffers, so one step touches about 1.3 GB and no kernel finds its
-inputs in the 256 MB Infinity Cache from the previous step.
+its own buffers, so one step touches 1.07 GB and no kernel finds its inputs
+in the 256 MB Infinity Cache from the previous step.
 
 Bytes are compulsory bytes: every input read once, every output written once,
 row-broadcast vectors once. The printed JSON line reports the whole-step
-throughput (GB/s), per-kernel us/call and GB/s, the roofline entry of the
-kernel that takes the most time, and the CPU oracle timed on a row sample.
+throughput (GB/s); per kernel, its mean duration launched back to back over
+rotating buffer sets (us_per_call, GB/s) and its marginal cost inside the
+step (us_in_step); the roofline entry of the kernel that takes the most
+time; and the CPU oracle timed on a row sample.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--blocks N]
 """
@@ -175,42 +177,59 @@ class Workload:
             fn()
 
 
-def time_steps(torch, wl, steps, per_kernel):
-    """Outer-event timing of `steps` steps. With per_kernel, one more event is
-    recorded after every launch (on torch's current stream, where the kernels
-    run): launch i lasts from the event before it to the event after it. All
-    events are created before the timed region, so the host only launches and
-    records inside it and stays ahead of the GPU."""
+def time_launches(torch, fns, reps):
+    """Mean time of `reps` launches issued back to back on torch's current
+    stream (where the kernels run), cycling through `fns`, between two events
+    recorded on that stream; plus the host wall time of the same region."""
     stream = torch.cuda.current_stream()
-    names = [n for n, _, _ in wl.launches]
-    n_marks = steps * (len(names) + 1) if per_kernel else 0
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_marks)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    labels = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    m = 0
-    for _ in range(steps):
-        if per_kernel:
-            events[m].record(stream)
-            labels.append(None)
-            m += 1
-        for n, _, fn in wl.launches:
-            fn()
-            if per_kernel:
-                events[m].record(stream)
-                labels.append(n)
-                m += 1
+    for i in range(reps):
+        fns[i % len(fns)]()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    kern = {n: [] for n in names}
-    for i in range(1, m):
-        if labels[i] is not None:
-            kern[labels[i]].append(events[i - 1].elapsed_time(events[i]))
-    return total_ms, wall, {n: sorted(t) for n, t in kern.items()}
+    return start.elapsed_time(end) / reps, wall / reps
+
+
+def time_steps(torch, wl, steps, skip=None):
+    """Mean ms per step (all launches of `wl` except `skip`, in order)."""
+    fns = [fn for n, _, fn in wl.launches if n != skip]
+
+    def step():
+        for fn in fns:
+            fn()
+
+    return time_launches(torch, [step], steps)
+
+
+ROTATION_BYTES = 640 << 20  # > 2x the 256 MB Infinity Cache
+
+
+def kernel_timings(torch, qe, wl, steps):
+    """Per launch: (a) its mean duration when launched back to back, cycling
+    through enough independent buffer sets that the sets together exceed
+    twice the Infinity Cache (so every launch reads from HBM), and (b) its
+    marginal cost inside the step: step time minus the time of the same step
+    without it."""
+    full, _ = time_steps(torch, wl, steps)
+    out = {}
+    for name, nbytes, fn in wl.launches:
+        # The extra Workload objects own the buffers their launches address:
+        # they stay referenced until the timing below has synchronised.
+        extra = [Workload(torch, qe, seed=1000 + i, names=(name,))
+                 for i in range(1, -(-ROTATION_BYTES // nbytes))]
+        sets = [fn] + [w.launches[0][2] for w in extra]
+        reps = max(100, 2 * len(sets))
+        for f in sets:
+            f()
+        iso_ms, _ = time_launches(torch, sets, reps)
+        without, _ = time_steps(torch, wl, steps, skip=name)
+        out[name] = {"iso_ms": iso_ms, "in_step_ms": full - without, "sets": len(sets), "reps": reps}
+        del sets, extra
+    return full, out
 
 
 # Source files that define each launch's kernel (for matching profiled traffic).
@@ -363,18 +382,18 @@ def main():
     wl = Workload(torch, qe, seed=0, names=names)
     for _ in range(args.warmup):
         wl.step()
-    total_ms, wall, _ = time_steps(torch, wl, args.steps, per_kernel=False)
-    _, _, kern = time_steps(torch, wl, args.steps, per_kernel=True)
-    ms = total_ms / args.steps
+    ms, wall = time_steps(torch, wl, args.steps)
     value = wl.step_bytes / (ms * 1e-3) / 1e9
+    _, timings = kernel_timings(torch, qe, wl, args.steps)
 
     kernels = {}
     for name, nbytes, _ in wl.launches:
-        t = kern[name]
-        mean = sum(t) / len(t)
-        kernels[name] = {"us_per_call": round(1e3 * mean, 3), "us_median": round(1e3 * t[len(t) // 2], 3),
-                         "bytes": nbytes, "gb_s": round(nbytes / (mean * 1e-3) / 1e9, 1),
-                         "pct_peak": round(100 * nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        t = timings[name]
+        iso, marg = t["iso_ms"], t["in_step_ms"]
+        kernels[name] = {"us_per_call": round(1e3 * iso, 3), "bytes": nbytes,
+                         "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
+                         "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                         "us_in_step": round(1e3 * marg, 3), "rotation_sets": t["sets"]}
     dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
     achieved = kernels[dom]["gb_s"]
     traffic = profiled_traffic(dom)
@@ -389,7 +408,7 @@ def main():
                    "launches_per_step": len(wl.launches), "step_bytes": wl.step_bytes,
                    "io": "bf16 in; bf16 + E4M3 / E2M1 out", "parallelism": "1 GPU"},
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "wall_ms_per_step": round(1e3 * wall, 4),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
