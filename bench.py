@@ -358,6 +358,8 @@ def main():
                     help="print the source hash of every launch's kernel and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step only, no per-kernel timing (for counter runs)")
     ap.add_argument("--blocks", type=int, default=0,
                     help="also time a Qwen-Image block sequence of this many blocks (e.g. 60)")
     args = ap.parse_args()
@@ -384,6 +386,10 @@ def main():
         wl.step()
     ms, wall = time_steps(torch, wl, args.steps)
     value = wl.step_bytes / (ms * 1e-3) / 1e9
+    if args.step_only:
+        print(json.dumps({"metric": METRIC, "value": round(value, 1), "unit": "GB/s",
+                          "ms_per_step": round(ms, 4), "steps": args.steps}), flush=True)
+        return
     _, timings = kernel_timings(torch, qe, wl, args.steps)
 
     kernels = {}

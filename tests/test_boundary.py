@@ -170,9 +170,11 @@ def test_refuses_launches_beyond_the_grid_limit(native):
     assert f(*([FAKE] * 10 + [big, 3072, 1e-6, None])) == native.DIT_ERR_UNSUPPORTED
     assert _qkv(L, img_rows=1 << 27) == native.DIT_ERR_UNSUPPORTED
     assert L.dit_bias_mul_add(FAKE, FAKE, None, FAKE, FAKE, big, 3072, None) == native.DIT_ERR_UNSUPPORTED
-    cat = L.dit_token_cat_quant
-    assert cat(native.DIT_QUANT_FP8_E4M3, FAKE, None, FAKE, 6144, FAKE2, 18432, big, FAKE,
-               None) == native.DIT_ERR_UNSUPPORTED
-    assert cat(native.DIT_QUANT_FP4_E2M1, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, big, FAKE,
-               None) == native.DIT_ERR_UNSUPPORTED
     assert "grid limit" in native.last_error()
+    # Token concatenation splits rows over several launches; its limits are
+    # the row count (2^31 - 128) and the row width (2^28).
+    cat = L.dit_token_cat_quant
+    assert cat(native.DIT_QUANT_FP8_E4M3, FAKE, None, FAKE, 6144, FAKE2, 18432, 1 << 31, FAKE,
+               None) == native.DIT_ERR_UNSUPPORTED
+    assert cat(native.DIT_QUANT_FP4_E2M1, FAKE, FAKE, FAKE, 1 << 28, FAKE2, 16, 4, FAKE,
+               None) == native.DIT_ERR_UNSUPPORTED

@@ -275,6 +275,7 @@ FP8_CASES = [
     (3, 6144, 0, 0.5, 2, False),
     (130, 16, 48, 0.4754464328, 3, False),
     (5, 6144, 2064, 0.05, 7, False),         # 1026 chunks: three tiles, the last ragged
+    (65540, 16, 16, 0.05, 8, False),         # rows beyond one launch's 65536
 ]
 
 
@@ -315,6 +316,7 @@ FP4_CASES = [
     (128, 6144, 0, "calibrated", 4, False),
     (129, 16, 16, "calibrated", 5, False),
     (19, 4112, 4112, "calibrated", 6, False),  # 514 groups: three tiles, the last ragged
+    (65540, 16, 16, "calibrated", 7, False),   # 65664 scale rows: two launches
 ]
 
 
