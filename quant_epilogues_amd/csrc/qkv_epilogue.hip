@@ -25,19 +25,23 @@
 namespace dit {
 namespace {
 
-// kPasses 4-head passes per wave (a wave covers 4 * kPasses heads).
+// kPasses 4-head passes per wave (a wave covers 4 * kPasses heads). Grid:
+// x = group of 4 joint tokens (one per wave), y = head group, z = part. The
+// wave index goes through readfirstlane so that everything derived from it
+// (token, stream, source and weight pointers) is known to be wave-uniform and
+// lives in scalar registers: the pointers then come from scalar loads of the
+// argument block instead of per-lane loads that would stall the wave before
+// its streaming loads are issued.
 template <int kPasses>
-__global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t units_per_part,
-                                                           uint32_t hblocks) {
+__global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a) {
     constexpr int kHeadsPerWave = 4 * kPasses;
     const int lane = threadIdx.x & 63;
     const int r = lane >> 4;  // head slot within a pass
     const int s = lane & 15;  // 8-element slice of the head
-    const uint32_t unit = blockIdx.x * 4u + (threadIdx.x >> 6);
-    if (unit >= units_per_part) return;
-    const int part = blockIdx.y;  // 0 = Q, 1 = K, 2 = V
-    const uint32_t hb = unit % hblocks;
-    const int64_t j = unit / hblocks;  // joint token
+    const int64_t j = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (j >= a.txt_rows + a.img_rows) return;
+    const int part = blockIdx.z;  // 0 = Q, 1 = K, 2 = V
+    const int hb = blockIdx.y;
 
     const bool is_txt = j < a.txt_rows;
     const int64_t i = is_txt ? j : j - a.txt_rows;
@@ -45,13 +49,16 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
                           i * (is_txt ? a.txt_stride : a.img_stride);
     uint16_t* dst = a.joint[part] + j * (int64_t)a.heads * kHeadDim;
 
+    // Head slots past the last head (heads not a multiple of 4 * kPasses)
+    // load the last head again, compute on it (the 16-lane row reduction
+    // never mixes rows) and skip their store: every load is unconditional.
     int head[kPasses];
     u32x4 xin[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-        head[p] = (int)hb * kHeadsPerWave + 4 * p + r;
-        xin[p] = head[p] < a.heads ? stream_load16(src + head[p] * kHeadDim + 8 * s)
-                                   : (u32x4){0, 0, 0, 0};
+        head[p] = hb * kHeadsPerWave + 4 * p + r;
+        const int hl = head[p] < a.heads ? head[p] : a.heads - 1;
+        xin[p] = stream_load16(src + hl * kHeadDim + 8 * s);
     }
 
     if (part == 2) {  // V: bit copy into the joint layout
@@ -73,9 +80,6 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
 
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-        // Inactive head slots compute on zeros (all 16 lanes of a row agree,
-        // so the row reduction never mixes live and dead lanes) and skip the
-        // store.
         float x[8];
         unpack8(xin[p], x);
         double ss = 0.0;
@@ -113,11 +117,10 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a, uint32_t u
 template <int kPasses>
 hipError_t launch_passes(const QkvArgs& a, hipStream_t stream) {
     const uint32_t hblocks = (uint32_t)((a.heads + 4 * kPasses - 1) / (4 * kPasses));
-    const uint64_t units = (uint64_t)(a.txt_rows + a.img_rows) * hblocks;
-    const uint64_t blocks = (units + 3) / 4;
+    const uint64_t blocks = ((uint64_t)(a.txt_rows + a.img_rows) + 3) / 4;
     if (blocks * 256 >= kMaxGridLanes) return kGridTooLarge;
-    hipLaunchKernelGGL(qkv_epilogue_kernel<kPasses>, dim3((unsigned)blocks, 3), dim3(256), 0, stream, a,
-                       (uint32_t)units, hblocks);
+    hipLaunchKernelGGL(qkv_epilogue_kernel<kPasses>, dim3((unsigned)blocks, hblocks, 3), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
