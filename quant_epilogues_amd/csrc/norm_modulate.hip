@@ -89,6 +89,8 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
         if (MODE != kPlain) rin[k] = ok[k] ? stream_load16(a.residual + base + 8 * c) : (u32x4){0, 0, 0, 0};
     }
 
+    const float inv = 1.0f / *a.input_scale;  // IEEE division
+
     // 2. Column vectors to fp32 in LDS, while the streaming loads are in flight.
     if (kLds) {
         for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
@@ -179,7 +181,6 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
     const double var = __builtin_fmax(s2 * inv_hidden - mean * mean, 0.0);
     const float factor = rsqrt_rn32(var + (double)a.eps);
     const float mean32 = (float)mean;
-    const float inv = 1.0f / *a.input_scale;  // IEEE division
 
     // 5. Modulate, quantise, store.
 #pragma unroll
