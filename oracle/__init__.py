@@ -18,7 +18,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_BUILT_PATH = os.path.join(_HERE, "liboracle.so")
+# The library lib() loads. DIT_ORACLE_LIB points it at another build of
+# oracle.c: the mutation tests load copies with planted mistakes this way to
+# show that the pinning tests catch them.
+_LIB_PATH = os.environ.get("DIT_ORACLE_LIB") or _BUILT_PATH
 
 # Plain C, IEEE binary32/binary64, no FMA contraction, no fast-math.
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
@@ -29,11 +33,16 @@ _lib = None
 
 def build(verbose: bool = False) -> str:
     """Compile oracle.c into liboracle.so next to it (always recompiles)."""
-    cmd = ["gcc", *CFLAGS, _SRC, "-o", _LIB_PATH, "-lm"]
+    return compile_source(_SRC, _BUILT_PATH, verbose)
+
+
+def compile_source(src: str, out: str, verbose: bool = False) -> str:
+    """Compile a copy of oracle.c (with oracle.h from this directory)."""
+    cmd = ["gcc", *CFLAGS, f"-I{_HERE}", src, "-o", out, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    return _LIB_PATH
+    return out
 
 
 def lib() -> ctypes.CDLL:

@@ -70,7 +70,10 @@ def test_bf16_of_exact_sum_matches_brute_force(oracle_mod):
     ca, cb = [], []
     for k in RNG.integers(0x3F00, 0x4A00, 300):
         mid = float((bf16_value(int(k)) + bf16_value(int(k) + 1)) / 2)
-        for nudge in (0.0, 2.0**-30, -(2.0**-30), 0.2080078125, -0.2080078125):
+        # 2^-60 and 2^-100 sit beyond binary64's reach of the midpoint, so the
+        # binary64 sum alone is a tie and only the TwoSum error breaks it.
+        for nudge in (0.0, 2.0**-30, -(2.0**-30), 0.2080078125, -0.2080078125,
+                      2.0**-60, -(2.0**-60), 2.0**-100, -(2.0**-100)):
             ca.append(mid)
             cb.append(nudge)
     a = np.concatenate([a, ca])

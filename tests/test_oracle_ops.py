@@ -173,6 +173,54 @@ def test_gated_residual_is_one_exact_rounding(oracle_mod):
                 assert r_out[i, j] == nearest_bf16_bits(exact), (i, j)
 
 
+def _constructed_gated_columns(n_ties=24):
+    """Columns (x, bias, gate, residual) of bf16 bits built so that each
+    rounding rule of the gated multiply-add decides the result:
+    - x = 1, bias = 2^-8 + 2^-10, gate = 3: rounding x + bias to bf16 first
+      gives 3 * 1.0078125 = 3.0234375, a tie that goes to 3.03125; without
+      that rounding the product is 3.017578125 -> 3.015625;
+    - products exactly on a bf16 midpoint with residual +-2^-40 (or 0): an
+      fp32 sum loses the residual and the tie goes to even, while the exact
+      sum rounds toward the residual's sign;
+    - the tie case printed on the sglang PR 37116 page."""
+    ties = _tie_products(n_ties)
+    cols = [(1.0, 2.0**-8 + 2.0**-10, 3.0, 0.0), (-1.0, -(2.0**-8 + 2.0**-10), 3.0, 0.0)]
+    for k, (xt, gt) in enumerate(ties):
+        nudge = (2.0**-40, -(2.0**-40), 0.0)[k % 3]
+        cols.append((float(bf2f([xt])[0]), 0.0, float(bf2f([gt])[0]), nudge))
+    with open(os.path.join(GOLDEN, "bias_mul_add_tie.json")) as f:
+        case = json.load(f)["inputs"]
+    cols.append((case["x"], case["bias"], case["gate"], case["residual"]))
+    x, bias, gate, res = (bfbits([c[i] for c in cols]) for i in range(4))
+    for i in range(4):  # every constructed value is a bf16 value
+        assert np.array_equal(bf2f((x, bias, gate, res)[i]).astype(np.float64), [c[i] for c in cols])
+    return x, bias, gate, res
+
+
+def _gated_reference(x, bias, gate, res):
+    """bf16(res + gate * bf16(RN32(x + bias))) with one exact final rounding."""
+    xb = bf2f(bfbits(bf2f(x) + bf2f(bias)))  # numpy fp32 add, torch bf16 RNE
+    return np.array([nearest_bf16_bits(bf16_value(r) + bf16_value(g) * Fraction(float(v)))
+                     for v, g, r in zip(xb, gate, res)], np.uint16)
+
+
+def test_gated_residual_constructed_rounding_cases(oracle_mod):
+    x, bias, gate, res = _constructed_gated_columns()
+    want = _gated_reference(x, bias, gate, res)
+    assert bf2f(want[:2]).tolist() == [3.03125, -3.03125]
+    zeros = np.zeros_like(x)
+    r_out, _, _, _ = oracle_mod.scale_residual_norm_modulate_fp8(
+        x.reshape(1, -1), bias, gate, res.reshape(1, -1), zeros, zeros, 1.0, 1e-6)
+    assert np.array_equal(r_out[0], want)
+
+
+def test_bias_mul_add_constructed_rounding_cases(oracle_mod):
+    x, bias, gate, res = _constructed_gated_columns()
+    want = _gated_reference(x, bias, gate, res)
+    y = oracle_mod.bias_mul_add(x.reshape(1, -1), bias, gate, res.reshape(1, -1))
+    assert np.array_equal(y[0], want)
+
+
 def test_scale_residual_equals_norm_of_residual_out(oracle_mod):
     inp = synth.scale_residual_inputs(rows=24, hidden=3072, seed=5, input_scale=0.02)
     b = synth.bf16_bits
