@@ -37,6 +37,7 @@ METRIC = "fused-epilogue HBM GB/s (% of MI355X peak) + µs/call at Qwen-Image sh
 
 QWEN_HIDDEN, IMG, TXT, HEADS, HEAD_DIM = 3072, 4096, 512, 24, 128
 FLUX_ROWS, FLUX_A, FLUX_B = 4608, 6144, 18432
+FLUX_HEADS = 48  # FLUX.2: hidden 6144 = 48 heads x 128
 
 
 def log(*a):
@@ -75,6 +76,9 @@ class Workload:
     """Device buffers and the launch list of one step. `names` selects launches."""
 
     ALL = ("norm_img", "norm_txt", "qkv", "sr_norm", "bma", "cat_fp8", "cat_fp4")
+    # Timed beside the step, not in it: the FLUX.2 shape of the QKV epilogue
+    # (4096 image + 512 text tokens, 48 heads, one shared [cos | sin] cache).
+    EXTRA = ("qkv_flux2",)
 
     def __init__(self, torch, qe, seed=0, names=ALL):
         import numpy as np
@@ -112,21 +116,29 @@ class Workload:
             return bytes_norm(rows, H), lambda: qe.dit_norm_modulate_fp8(
                 *p, rows, H, 1e-6, stream=st)
 
-        def qkv():
+        def qkv(heads=HEADS, shared_cache=False):
+            W = heads * HEAD_DIM
             img, txt = randn(IMG, 3 * W), randn(TXT, 3 * W)
             ws = [randn(HEAD_DIM, std=0.05, mean=1.0) for _ in range(4)]
             tc, ts = synth.rope_tables(np.arange(TXT), HEAD_DIM)
             ic, is_ = synth.rope_tables(np.arange(TXT, TXT + IMG), HEAD_DIM)
-            tc, ts, ic, is_ = (torch.from_numpy(a).to(dev) for a in (tc, ts, ic, is_))
-            jq, jk, jv = (empty(IMG + TXT, HEADS, HEAD_DIM) for _ in range(3))
+            half = HEAD_DIM // 2
+            if shared_cache:  # one [txt + img, 128] cache, rows [cos | sin] in joint order
+                cache = torch.from_numpy(np.concatenate(
+                    [np.concatenate([tc, ts], 1), np.concatenate([ic, is_], 1)])).to(dev)
+                tables, stride = (cache[TXT:, :half], cache[TXT:, half:], cache[:TXT, :half],
+                                  cache[:TXT, half:]), 2 * half
+            else:
+                tables, stride = tuple(torch.from_numpy(a).to(dev) for a in (ic, is_, tc, ts)), half
+            jq, jk, jv = (empty(IMG + TXT, heads, HEAD_DIM) for _ in range(3))
             o = P(jq, jk, jv)
             i3 = P(img[:, :W], img[:, W:2 * W], img[:, 2 * W:])
             t3 = P(txt[:, :W], txt[:, W:2 * W], txt[:, 2 * W:])
             w4 = P(*ws)
-            r4 = P(ic, is_, tc, ts)
-            return bytes_qkv(IMG + TXT, HEADS, HEAD_DIM), lambda: qe.dit_qkv_epilogue(
-                *o, *i3, IMG, 3 * W, *t3, TXT, 3 * W, *w4, *r4, HEADS, HEAD_DIM, 1e-6, 1e-6,
-                stream=st)
+            r4 = P(*tables)
+            return bytes_qkv(IMG + TXT, heads, HEAD_DIM), lambda: qe.dit_qkv_epilogue(
+                *o, *i3, IMG, 3 * W, *t3, TXT, 3 * W, *w4, *r4, stride, heads, HEAD_DIM,
+                1e-6, 1e-6, stream=st)
 
         def sr_norm():
             x, res = randn(IMG, H), randn(IMG, H)
@@ -165,6 +177,7 @@ class Workload:
             "sr_norm": sr_norm, "bma": bma,
             "cat_fp8": lambda: cat(qe.DIT_QUANT_FP8_E4M3),
             "cat_fp4": lambda: cat(qe.DIT_QUANT_FP4_E2M1),
+            "qkv_flux2": lambda: qkv(heads=FLUX_HEADS, shared_cache=True),
         }
         self.launches = []  # (name, compulsory bytes, launch)
         for n in names:
@@ -208,13 +221,13 @@ def time_steps(torch, wl, steps, skip=None):
 ROTATION_BYTES = 640 << 20  # > 2x the 256 MB Infinity Cache
 
 
-def kernel_timings(torch, qe, wl, steps):
+def kernel_timings(torch, qe, wl, steps, in_step=True):
     """Per launch: (a) its mean duration when launched back to back, cycling
     through enough independent buffer sets that the sets together exceed
     twice the Infinity Cache (so every launch reads from HBM), and (b) its
     marginal cost inside the step: step time minus the time of the same step
     without it."""
-    full, _ = time_steps(torch, wl, steps)
+    full = time_steps(torch, wl, steps)[0] if in_step else None
     out = {}
     for name, nbytes, fn in wl.launches:
         # The extra Workload objects own the buffers their launches address:
@@ -226,8 +239,8 @@ def kernel_timings(torch, qe, wl, steps):
         for f in sets:
             f()
         iso_ms, _ = time_launches(torch, sets, reps)
-        without, _ = time_steps(torch, wl, steps, skip=name)
-        out[name] = {"iso_ms": iso_ms, "in_step_ms": full - without, "sets": len(sets), "reps": reps}
+        marg = full - time_steps(torch, wl, steps, skip=name)[0] if in_step else None
+        out[name] = {"iso_ms": iso_ms, "in_step_ms": marg, "sets": len(sets), "reps": reps}
         del sets, extra
     return full, out
 
@@ -236,7 +249,7 @@ def kernel_timings(torch, qe, wl, steps):
 KERNEL_SOURCES = {
     "norm_img": "norm_modulate.hip", "norm_txt": "norm_modulate.hip", "sr_norm": "norm_modulate.hip",
     "qkv": "qkv_epilogue.hip", "bma": "bias_mul_add.hip", "cat_fp8": "token_cat_quant.hip",
-    "cat_fp4": "token_cat_quant.hip",
+    "cat_fp4": "token_cat_quant.hip", "qkv_flux2": "qkv_epilogue.hip",
 }
 
 
@@ -400,6 +413,17 @@ def main():
                          "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
                          "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                          "us_in_step": round(1e3 * marg, 3), "rotation_sets": t["sets"]}
+    extra = {}
+    if not args.only:
+        ex = Workload(torch, qe, seed=0, names=Workload.EXTRA)
+        _, ext = kernel_timings(torch, qe, ex, args.steps, in_step=False)
+        for name, nbytes, _ in ex.launches:
+            iso = ext[name]["iso_ms"]
+            extra[name] = {"us_per_call": round(1e3 * iso, 3), "bytes": nbytes,
+                           "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
+                           "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                           "rotation_sets": ext[name]["sets"]}
+        del ex
     dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
     achieved = kernels[dom]["gb_s"]
     traffic = profiled_traffic(dom)
@@ -416,6 +440,7 @@ def main():
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "wall_ms_per_step": round(1e3 * wall, 4),
         "kernels": kernels,
+        "extra_kernels": extra,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": kernels[dom]["bytes"]},

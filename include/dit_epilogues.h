@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 1
+#define DIT_ABI_VERSION 2
 
 typedef enum dit_status {
     DIT_OK = 0,
@@ -133,14 +133,20 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
  *   txt_q, txt_k, txt_v  the same for the text stream
  *   *_row_stride  in ELEMENTS; >= heads * head_dim and a multiple of 8
  *   img_q_w, img_k_w, txt_q_w, txt_k_w  [head_dim] bf16 RMSNorm weights
- *   img_cos, img_sin  [img_rows, head_dim / 2] fp32; txt_cos, txt_sin
- *       [txt_rows, head_dim / 2] fp32. Pair (2i, 2i+1) of a row rotates by the
- *       angle whose cos/sin are entry i of that row:
+ *   img_cos, img_sin  fp32 tables with one row of head_dim / 2 entries per
+ *       image row; txt_cos, txt_sin the same per text row. Pair (2i, 2i+1) of
+ *       a row rotates by the angle whose cos/sin are entry i of that row:
  *       (a, b) -> (a cos - b sin, b cos + a sin)
+ *   rope_row_stride  elements between consecutive rows of all four tables;
+ *       >= head_dim / 2 and a multiple of 4. head_dim / 2 for dense tables;
+ *       head_dim for one shared cache whose rows hold [cos | sin] (pass
+ *       img_cos = cache + txt_rows * head_dim, img_sin = img_cos + head_dim / 2,
+ *       txt_cos = cache, txt_sin = cache + head_dim / 2), as the FLUX.2 variant
+ *       on the sglang PR 37162 page takes one cos/sin cache for both streams
  *   img_eps, txt_eps  RMSNorm epsilons
  *
- * head_dim must be 128 (else DIT_ERR_UNSUPPORTED); heads in [1, 64].
- * Either stream may have zero rows.
+ * head_dim must be 128 (else DIT_ERR_UNSUPPORTED); heads in [1, 64] (24 for
+ * Qwen-Image, 48 for FLUX.2). Either stream may have zero rows.
  */
 int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v,
                      const void* img_q, const void* img_k, const void* img_v,
@@ -150,7 +156,7 @@ int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v,
                      const void* img_q_w, const void* img_k_w,
                      const void* txt_q_w, const void* txt_k_w,
                      const float* img_cos, const float* img_sin,
-                     const float* txt_cos, const float* txt_sin,
+                     const float* txt_cos, const float* txt_sin, int64_t rope_row_stride,
                      int32_t heads, int32_t head_dim, float img_eps, float txt_eps,
                      void* stream);
 

@@ -79,7 +79,9 @@ def qkv_epilogue(img_q, img_k, img_v, txt_q, txt_k, txt_v, img_q_w, img_k_w, txt
                  img_eps: float = 1e-6, txt_eps: float = 1e-6, head_dim: int = 128):
     """Q/K RMSNorm + interleaved RoPE + V copy into joint [text, image] buffers.
     img_*/txt_* are [rows, heads * head_dim] views (e.g. column slices of the
-    packed QKV GEMM output). Returns (joint_q, joint_k, joint_v), each
+    packed QKV GEMM output). The four fp32 cos/sin tables are [rows, head_dim/2]
+    views sharing one row stride (dense tables, or column halves of one
+    [cos | sin] cache). Returns (joint_q, joint_k, joint_v), each
     [txt_rows + img_rows, heads, head_dim]."""
     width = heads * head_dim
     img_stride = _row_view(img_q, width, "img_q")
@@ -88,13 +90,21 @@ def qkv_epilogue(img_q, img_k, img_v, txt_q, txt_k, txt_v, img_q_w, img_k_w, txt
                      (txt_k, "txt_k", txt_stride), (txt_v, "txt_v", txt_stride)):
         if _row_view(t, width, n) != st:
             raise ValueError(f"{n} must share its stream's row stride")
+    tables = [t for t, rows in ((img_cos, img_q.shape[0]), (img_sin, img_q.shape[0]),
+                                (txt_cos, txt_q.shape[0]), (txt_sin, txt_q.shape[0])) if rows]
+    for t in tables:
+        if t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1 or t.shape[1] != head_dim // 2:
+            raise ValueError("cos/sin tables must be fp32 [rows, head_dim/2] row views")
+    rope_stride = tables[0].stride(0) if tables else head_dim // 2
+    if any(t.stride(0) != rope_stride for t in tables):
+        raise ValueError("the cos/sin tables must share one row stride")
     n_tok = img_q.shape[0] + txt_q.shape[0]
     out = [torch.empty((n_tok, heads, head_dim), dtype=torch.bfloat16, device=img_q.device)
            for _ in range(3)]
     dit_qkv_epilogue(out[0], out[1], out[2], img_q, img_k, img_v, img_q.shape[0], img_stride,
                      txt_q, txt_k, txt_v, txt_q.shape[0], txt_stride, img_q_w, img_k_w,
-                     txt_q_w, txt_k_w, img_cos, img_sin, txt_cos, txt_sin, heads, head_dim,
-                     img_eps, txt_eps)
+                     txt_q_w, txt_k_w, img_cos, img_sin, txt_cos, txt_sin, rope_stride, heads,
+                     head_dim, img_eps, txt_eps)
     return tuple(out)
 
 

@@ -39,8 +39,8 @@ _SIGNATURES = {
     "dit_scale_residual_norm_modulate_fp8":
         (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
     "dit_qkv_epilogue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _I64,
-                                        _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F,
-                                        _F, _P]),
+                                        _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32,
+                                        _F, _F, _P]),
     "dit_bias_mul_add": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _P]),
     "dit_token_cat_quant": (ctypes.c_int, [_I32, _P, _P, _P, _I64, _P, _I64, _I64, _P, _P]),
 }
@@ -129,14 +129,14 @@ def dit_scale_residual_norm_modulate_fp8(residual_out, y, q, x, bias, gate, resi
 
 def dit_qkv_epilogue(joint_q, joint_k, joint_v, img_q, img_k, img_v, img_rows, img_row_stride,
                      txt_q, txt_k, txt_v, txt_rows, txt_row_stride, img_q_w, img_k_w, txt_q_w,
-                     txt_k_w, img_cos, img_sin, txt_cos, txt_sin, heads, head_dim, img_eps,
-                     txt_eps, stream=None) -> None:
+                     txt_k_w, img_cos, img_sin, txt_cos, txt_sin, rope_row_stride, heads,
+                     head_dim, img_eps, txt_eps, stream=None) -> None:
     _check(lib().dit_qkv_epilogue(
         _ptr(joint_q), _ptr(joint_k), _ptr(joint_v), _ptr(img_q), _ptr(img_k), _ptr(img_v),
         img_rows, img_row_stride, _ptr(txt_q), _ptr(txt_k), _ptr(txt_v), txt_rows,
         txt_row_stride, _ptr(img_q_w), _ptr(img_k_w), _ptr(txt_q_w), _ptr(txt_k_w),
-        _ptr(img_cos), _ptr(img_sin), _ptr(txt_cos), _ptr(txt_sin), heads, head_dim, img_eps,
-        txt_eps, _stream(stream, joint_q)))
+        _ptr(img_cos), _ptr(img_sin), _ptr(txt_cos), _ptr(txt_sin), rope_row_stride, heads,
+        head_dim, img_eps, txt_eps, _stream(stream, joint_q)))
 
 
 def dit_bias_mul_add(y, x, bias, gate, residual, rows, hidden, stream=None) -> None:

@@ -144,8 +144,9 @@ int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v, const void* im
                      const void* txt_v, int64_t txt_rows, int64_t txt_row_stride,
                      const void* img_q_w, const void* img_k_w, const void* txt_q_w,
                      const void* txt_k_w, const float* img_cos, const float* img_sin,
-                     const float* txt_cos, const float* txt_sin, int32_t heads,
-                     int32_t head_dim, float img_eps, float txt_eps, void* stream) {
+                     const float* txt_cos, const float* txt_sin, int64_t rope_row_stride,
+                     int32_t heads, int32_t head_dim, float img_eps, float txt_eps,
+                     void* stream) {
     const char* fn = "dit_qkv_epilogue";
     if (img_rows < 0 || txt_rows < 0)
         return fail(DIT_ERR_SHAPE, "%s: row counts must be >= 0", fn);
@@ -165,6 +166,9 @@ int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v, const void* im
         (txt_rows > 0 && (txt_row_stride < width || txt_row_stride % 8 != 0)))
         return fail(DIT_ERR_SHAPE, "%s: row strides must be >= heads*head_dim (%lld) and a multiple of 8",
                     fn, (long long)width);
+    if (rope_row_stride < head_dim / 2 || rope_row_stride % 4 != 0)
+        return fail(DIT_ERR_SHAPE, "%s: rope_row_stride (%lld) must be >= head_dim/2 and a multiple of 4",
+                    fn, (long long)rope_row_stride);
     const int64_t hblocks = (heads + dit::kQkvHeadsPerWave - 1) / dit::kQkvHeadsPerWave;
     if (img_rows > kMaxRows || txt_rows > kMaxRows || (img_rows + txt_rows) * hblocks >= (int64_t(1) << 32) - 4)
         return fail(DIT_ERR_UNSUPPORTED, "%s: too many tokens", fn);
@@ -200,6 +204,7 @@ int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v, const void* im
     a.img_sin = img_sin;
     a.txt_cos = txt_cos;
     a.txt_sin = txt_sin;
+    a.rope_stride = rope_row_stride;
     a.img_rows = img_rows;
     a.img_stride = img_row_stride;
     a.txt_rows = txt_rows;

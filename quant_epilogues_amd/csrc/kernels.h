@@ -43,6 +43,7 @@ struct QkvArgs {
     const float* img_sin;
     const float* txt_cos;
     const float* txt_sin;
+    int64_t rope_stride;           // elements between rows of the cos / sin tables
     int64_t img_rows, img_stride;  // stride in elements
     int64_t txt_rows, txt_stride;
     int32_t heads;

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a) {
 
     float w[8];
     unpack8(load16((is_txt ? a.txt_w[part] : a.img_w[part]) + 8 * s), w);
-    const float* cos_row = (is_txt ? a.txt_cos : a.img_cos) + i * (kHeadDim / 2) + 4 * s;
-    const float* sin_row = (is_txt ? a.txt_sin : a.img_sin) + i * (kHeadDim / 2) + 4 * s;
+    const float* cos_row = (is_txt ? a.txt_cos : a.img_cos) + i * a.rope_stride + 4 * s;
+    const float* sin_row = (is_txt ? a.txt_sin : a.img_sin) + i * a.rope_stride + 4 * s;
     const float4 c4 = *reinterpret_cast<const float4*>(cos_row);
     const float4 s4 = *reinterpret_cast<const float4*>(sin_row);
     const double cs[4] = {c4.x, c4.y, c4.z, c4.w};

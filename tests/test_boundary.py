@@ -104,12 +104,12 @@ def test_scale_residual_refusals(native):
 
 def _qkv(L, **kw):
     a = dict(heads=24, head_dim=128, img_rows=8, txt_rows=2, img_stride=9216, txt_stride=9216,
-             img_q=FAKE, txt_q=FAKE, jq=FAKE, img_cos=FAKE)
+             img_q=FAKE, txt_q=FAKE, jq=FAKE, img_cos=FAKE, rope_stride=64)
     a.update(kw)
     return L.dit_qkv_epilogue(a["jq"], FAKE, FAKE, a["img_q"], FAKE, FAKE, a["img_rows"],
                               a["img_stride"], a["txt_q"], FAKE, FAKE, a["txt_rows"],
                               a["txt_stride"], FAKE, FAKE, FAKE, FAKE, a["img_cos"], FAKE, FAKE,
-                              FAKE, a["heads"], a["head_dim"], 1e-6, 1e-6, None)
+                              FAKE, a["rope_stride"], a["heads"], a["head_dim"], 1e-6, 1e-6, None)
 
 
 def test_qkv_refusals(native):
@@ -123,6 +123,9 @@ def test_qkv_refusals(native):
     assert _qkv(L, jq=None) == native.DIT_ERR_NULL
     assert _qkv(L, img_q=None) == native.DIT_ERR_NULL
     assert _qkv(L, img_cos=FAKE + 4) == native.DIT_ERR_ALIGN
+    assert _qkv(L, rope_stride=32) == native.DIT_ERR_SHAPE  # shorter than head_dim / 2
+    assert _qkv(L, rope_stride=66) == native.DIT_ERR_SHAPE  # rows not 16-byte aligned
+    assert _qkv(L, rope_stride=128, img_rows=0, txt_rows=0) == native.DIT_OK
     # A stream with no rows needs no pointers.
     assert _qkv(L, img_rows=0, txt_rows=0, img_q=None, txt_q=None) == native.DIT_OK
 

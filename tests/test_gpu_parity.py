@@ -156,17 +156,20 @@ def test_fp8_split_equals_fused_on_gpu(qe):
 # ---------------------------------------------------------------------------
 
 QKV_CASES = [
-    (4096, 512, 24, 0),   # Qwen-Image 1024^2: 4096 image + 512 text tokens
-    (5, 3, 3, 1),         # heads not a multiple of 4
-    (7, 2, 24, 2),
-    (3, 4, 48, 3),        # FLUX.2 head count: two 24-head blocks
-    (2, 1, 64, 4),
-    (6, 0, 24, 5),        # image only
-    (0, 5, 5, 6),         # text only
+    (4096, 512, 24, 0, False),   # Qwen-Image 1024^2: 4096 image + 512 text tokens
+    (5, 3, 3, 1, False),         # heads not a multiple of 4
+    (7, 2, 24, 2, False),
+    (3, 4, 48, 3, True),         # FLUX.2 head count (two 24-head waves), shared cache
+    (2, 1, 64, 4, False),
+    (6, 0, 24, 5, True),         # image only
+    (0, 5, 5, 6, True),          # text only
 ]
 
 
-def _run_qkv(qe, inp, contiguous=False):
+def _run_qkv(qe, inp, contiguous=False, shared_cache=False):
+    """Runs the C entry point. shared_cache: the four cos/sin tables are views
+    of one [txt + img, 128] fp32 cache whose rows hold [cos | sin] in joint
+    order (row stride 128), as the FLUX.2 variant binds them."""
     views = {}
     for stream in ("img", "txt"):
         qkv = dev(inp.img_qkv if stream == "img" else inp.txt_qkv)
@@ -175,34 +178,72 @@ def _run_qkv(qe, inp, contiguous=False):
         if contiguous:
             vs = tuple(t.contiguous() for t in vs)
         views[stream] = vs
-    n = inp.img_qkv.shape[0] + inp.txt_qkv.shape[0]
+    n_txt, n = inp.txt_qkv.shape[0], inp.img_qkv.shape[0] + inp.txt_qkv.shape[0]
     outs = [Guarded((n, inp.heads, inp.head_dim), torch.bfloat16) for _ in range(3)]
-    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    half = inp.head_dim // 2
+    if shared_cache:
+        cache = np.concatenate([np.concatenate([inp.txt_cos, inp.txt_sin], axis=1),
+                                np.concatenate([inp.img_cos, inp.img_sin], axis=1)])
+        cache = torch.from_numpy(np.ascontiguousarray(cache, np.float32)).cuda()
+        tables = (cache[n_txt:, :half], cache[n_txt:, half:], cache[:n_txt, :half],
+                  cache[:n_txt, half:])
+        stride = 2 * half
+    else:
+        tables = tuple(torch.from_numpy(np.ascontiguousarray(t)).cuda()
+                       for t in (inp.img_cos, inp.img_sin, inp.txt_cos, inp.txt_sin))
+        stride = half
     (iq, ik, iv), (tq, tk, tv) = views["img"], views["txt"]
     qe.dit_qkv_epilogue(outs[0].t, outs[1].t, outs[2].t, iq, ik, iv, iq.shape[0], iq.stride(0),
                         tq, tk, tv, tq.shape[0], tq.stride(0), dev(inp.img_q_w),
-                        dev(inp.img_k_w), dev(inp.txt_q_w), dev(inp.txt_k_w), f32(inp.img_cos),
-                        f32(inp.img_sin), f32(inp.txt_cos), f32(inp.txt_sin), inp.heads,
-                        inp.head_dim, inp.img_eps, inp.txt_eps)
+                        dev(inp.img_k_w), dev(inp.txt_q_w), dev(inp.txt_k_w), *tables, stride,
+                        inp.heads, inp.head_dim, inp.img_eps, inp.txt_eps)
     torch.cuda.synchronize()
     for o, name in zip(outs, "qkv"):
         o.check("joint_" + name)
     return [o.bits() for o in outs]
 
 
-@pytest.mark.parametrize("img_rows,txt_rows,heads,seed", QKV_CASES)
-def test_qkv_epilogue(qe, oracle_mod, img_rows, txt_rows, heads, seed):
-    _print_case("qkv_epilogue", img_rows, txt_rows, heads, seed)
+def _oracle_qkv(oracle_mod, inp, img_sel=None, txt_sel=None):
+    """The oracle on all rows, or on the selected image / text rows (joint
+    output rows: the selected text rows, then the selected image rows)."""
+    i_sel = np.arange(inp.img_qkv.shape[0]) if img_sel is None else img_sel
+    t_sel = np.arange(inp.txt_qkv.shape[0]) if txt_sel is None else txt_sel
+    return oracle_mod.qkv_epilogue_packed(
+        bits(inp.img_qkv)[i_sel], bits(inp.txt_qkv)[t_sel], bits(inp.img_q_w),
+        bits(inp.img_k_w), bits(inp.txt_q_w), bits(inp.txt_k_w), inp.img_cos[i_sel],
+        inp.img_sin[i_sel], inp.txt_cos[t_sel], inp.txt_sin[t_sel], inp.heads, inp.head_dim,
+        inp.img_eps, inp.txt_eps)
+
+
+@pytest.mark.parametrize("img_rows,txt_rows,heads,seed,shared", QKV_CASES)
+def test_qkv_epilogue(qe, oracle_mod, img_rows, txt_rows, heads, seed, shared):
+    _print_case("qkv_epilogue", img_rows, txt_rows, heads, seed, shared)
     inp = synth.qkv_inputs(img_rows, txt_rows, heads, 128, seed=seed, img_eps=1e-6,
                            txt_eps=1e-5)
-    gq, gk, gv = _run_qkv(qe, inp)
-    rq, rk, rv = oracle_mod.qkv_epilogue_packed(
-        bits(inp.img_qkv), bits(inp.txt_qkv), bits(inp.img_q_w), bits(inp.img_k_w),
-        bits(inp.txt_q_w), bits(inp.txt_k_w), inp.img_cos, inp.img_sin, inp.txt_cos,
-        inp.txt_sin, inp.heads, inp.head_dim, inp.img_eps, inp.txt_eps)
+    gq, gk, gv = _run_qkv(qe, inp, shared_cache=shared)
+    rq, rk, rv = _oracle_qkv(oracle_mod, inp)
     eq = check_bf16("joint_q", gq, rq)
     ek = check_bf16("joint_k", gk, rk)
     check_exact("joint_v", gv, rv)
+    print(f"exact: q {eq:.6f} k {ek:.6f}")
+
+
+def test_qkv_epilogue_flux2_full_shape(qe, oracle_mod):
+    """FLUX.2 at 1024^2: 4096 image + 512 text tokens, 48 heads, one shared
+    [cos | sin] cache; the oracle checks sampled tokens of both streams."""
+    _print_case("qkv_epilogue flux2", 4096, 512, 48, 11, True)
+    inp = synth.qkv_inputs(4096, 512, 48, 128, seed=11, img_eps=1e-6, txt_eps=1e-6)
+    gq, gk, gv = _run_qkv(qe, inp, shared_cache=True)
+    rng = np.random.default_rng(11)
+    img_sel = np.unique(np.concatenate([[0, 1, 2, 4094, 4095], rng.integers(0, 4096, 24)]))
+    txt_sel = np.unique(np.concatenate([[0, 1, 510, 511], rng.integers(0, 512, 8)]))
+    rq, rk, rv = _oracle_qkv(oracle_mod, inp, img_sel, txt_sel)
+    rows = np.concatenate([txt_sel, 512 + img_sel])
+    eq = check_bf16("joint_q", gq[rows], rq)
+    ek = check_bf16("joint_k", gk[rows], rk)
+    check_exact("joint_v", gv[rows], rv)
+    check_exact("joint_v (all rows)", gv, np.concatenate(
+        [bits(inp.txt_qkv)[:, 2 * inp.width:], bits(inp.img_qkv)[:, 2 * inp.width:]]).reshape(gv.shape))
     print(f"exact: q {eq:.6f} k {ek:.6f}")
 
 
@@ -210,8 +251,9 @@ def test_qkv_contiguous_equals_strided(qe):
     inp = synth.qkv_inputs(64, 16, 24, 128, seed=9)
     a = _run_qkv(qe, inp, contiguous=False)
     b = _run_qkv(qe, inp, contiguous=True)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    c = _run_qkv(qe, inp, shared_cache=True)
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(x, y) and np.array_equal(x, z)
 
 
 # ---------------------------------------------------------------------------
@@ -343,6 +385,35 @@ def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed
     ec, es = check_fp4("fp4", gp[sel], gs_sel, rp, rs_full, s_pre, pre, x, gv, e4m3_table,
                        oracle_mod.e2m1_encode)
     print(f"exact: codes {ec:.6f} scales {es:.6f}")
+
+
+def test_token_cat_fp4_all_bf16_values_unit_scale(qe, oracle_mod):
+    """Every bf16 value in [-6, 6] through the FP4 path at unit scale: each
+    16-element group holds +-6 (so amax / 6 * g = 1 with g = 1, the scale code
+    is 0x38 and the element scale is exactly 1) and 15 test values, so every
+    code is the E2M1 rounding of a bf16 value itself."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[(pats & 0x7FFF) <= 0x40C0]  # |x| <= 6, including -0 and subnormals
+    pats = np.concatenate([pats, np.zeros((-pats.size) % 15, np.uint16)]).reshape(-1, 15)
+    anchor = np.where(np.arange(pats.shape[0]) % 2 == 0, 0x40C0, 0xC0C0).astype(np.uint16)
+    groups = np.concatenate([anchor[:, None], pats], axis=1)  # [n_groups, 16]
+    groups = np.concatenate([groups, np.tile(groups[:1], ((-groups.shape[0]) % 64, 1))])
+    rows_bits = groups.reshape(-1, 64 * 16)  # 1024 columns per row
+    rows = rows_bits.shape[0]
+    a = torch.from_numpy(rows_bits.view(np.int16)).view(torch.bfloat16)
+    packed, scales = qe.token_cat_quant(qe.DIT_QUANT_FP4_E2M1, dev(a), None, dscalar(1.0))
+    rp, rs, _, _ = oracle_mod.token_cat_fp4(rows_bits, np.zeros((rows, 0), np.uint16), 1.0)
+    gs = scales.cpu().numpy()
+    assert np.all(gs[:rows] == 0x38) and np.all(gs[rows:] == 0)
+    assert np.all(rs[:rows] == 0x38) and np.all(rs[rows:] == 0)
+    check_exact("codes", packed.cpu().numpy(), rp)
+    # The codes are the E2M1 rounding of each value itself.
+    x = oracle_mod.f32_from_bf16(rows_bits)
+    want = oracle_mod.e2m1_encode(x)
+    got = packed.cpu().numpy()
+    nib = np.stack([got & 0xF, got >> 4], axis=-1).reshape(rows, -1)
+    same = (nib == want) | (((nib | want) & 7) == 0)  # +0 and -0 both encode zero
+    assert same.all()
 
 
 # ---------------------------------------------------------------------------
