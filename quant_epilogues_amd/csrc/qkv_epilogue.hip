@@ -25,23 +25,26 @@
 namespace dit {
 namespace {
 
-// kPasses 4-head passes per wave (a wave covers 4 * kPasses heads). Grid:
-// x = group of 4 joint tokens (one per wave), y = head group, z = part. The
-// wave index goes through readfirstlane so that everything derived from it
-// (token, stream, source and weight pointers) is known to be wave-uniform and
-// lives in scalar registers: the pointers then come from scalar loads of the
-// argument block instead of per-lane loads that would stall the wave before
-// its streaming loads are issued.
-template <int kPasses>
+// kPasses 4-head passes per wave (a wave covers 4 * kPasses heads); a token
+// has kHBlocks such head groups. Grid: x = group of 4 units, y = part; unit
+// u of a part is head group u % kHBlocks of joint token u / kHBlocks, so
+// consecutive waves read consecutive memory. The wave index goes through
+// readfirstlane so that everything derived from it (token, stream, source
+// and weight pointers) is known to be wave-uniform and lives in scalar
+// registers: the pointers then come from scalar loads of the argument block
+// instead of per-lane loads that would stall the wave before its streaming
+// loads are issued.
+template <int kPasses, int kHBlocks>
 __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a) {
     constexpr int kHeadsPerWave = 4 * kPasses;
     const int lane = threadIdx.x & 63;
     const int r = lane >> 4;  // head slot within a pass
     const int s = lane & 15;  // 8-element slice of the head
-    const int64_t j = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t unit = (uint64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t j = (int64_t)(unit / kHBlocks);
+    const int hb = (int)(unit % kHBlocks);
     if (j >= a.txt_rows + a.img_rows) return;
-    const int part = blockIdx.z;  // 0 = Q, 1 = K, 2 = V
-    const int hb = blockIdx.y;
+    const int part = blockIdx.y;  // 0 = Q, 1 = K, 2 = V
 
     const bool is_txt = j < a.txt_rows;
     const int64_t i = is_txt ? j : j - a.txt_rows;
@@ -114,14 +117,24 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a) {
     }
 }
 
+template <int kPasses, int kHBlocks>
+hipError_t launch_groups(const QkvArgs& a, hipStream_t stream) {
+    const uint64_t units = (uint64_t)(a.txt_rows + a.img_rows) * kHBlocks;
+    const uint64_t blocks = (units + 3) / 4;
+    if (blocks * 256 >= kMaxGridLanes) return kGridTooLarge;
+    hipLaunchKernelGGL((qkv_epilogue_kernel<kPasses, kHBlocks>), dim3((unsigned)blocks, 3),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int kPasses>
 hipError_t launch_passes(const QkvArgs& a, hipStream_t stream) {
-    const uint32_t hblocks = (uint32_t)((a.heads + 4 * kPasses - 1) / (4 * kPasses));
-    const uint64_t blocks = ((uint64_t)(a.txt_rows + a.img_rows) + 3) / 4;
-    if (blocks * 256 >= kMaxGridLanes) return kGridTooLarge;
-    hipLaunchKernelGGL(qkv_epilogue_kernel<kPasses>, dim3((unsigned)blocks, hblocks, 3), dim3(256), 0,
-                       stream, a);
-    return hipGetLastError();
+    static_assert(kMaxHeads <= 3 * 4 * kPasses, "head groups beyond three need an instance");
+    switch ((a.heads + 4 * kPasses - 1) / (4 * kPasses)) {
+        case 1: return launch_groups<kPasses, 1>(a, stream);
+        case 2: return launch_groups<kPasses, 2>(a, stream);
+        default: return launch_groups<kPasses, 3>(a, stream);
+    }
 }
 
 }  // namespace
