@@ -46,12 +46,12 @@ def log(*a):
 
 # ---- compulsory bytes per launch ------------------------------------------------
 
-def bytes_norm(rows, hidden):
-    return 5 * rows * hidden + 4 * hidden + 4
+def bytes_norm(rows, hidden, y=True, q=True):
+    return (2 + 2 * y + q) * rows * hidden + 4 * hidden + 4 * q
 
 
-def bytes_sr(rows, hidden, bias=True):
-    return 9 * rows * hidden + (8 if bias else 6) * hidden + 4
+def bytes_sr(rows, hidden, bias=True, y=True, q=True):
+    return (6 + 2 * y + q) * rows * hidden + (8 if bias else 6) * hidden + 4 * q
 
 
 def bytes_qkv(n_tok, heads, head_dim):
@@ -77,8 +77,10 @@ class Workload:
 
     ALL = ("norm_img", "norm_txt", "qkv", "sr_norm", "bma", "cat_fp8", "cat_fp4")
     # Timed beside the step, not in it: the FLUX.2 shape of the QKV epilogue
-    # (4096 image + 512 text tokens, 48 heads, one shared [cos | sin] cache).
-    EXTRA = ("qkv_flux2",)
+    # (4096 image + 512 text tokens, 48 heads, one shared [cos | sin] cache),
+    # the FP8-only LayerNorm + modulation at the FLUX.2 shape (4608 x 6144, no
+    # bf16 output) and the bf16-only bias + gated-residual norm (no FP8).
+    EXTRA = ("qkv_flux2", "norm_flux2_fp8", "sr_norm_bf16")
 
     def __init__(self, torch, qe, seed=0, names=ALL):
         import numpy as np
@@ -109,12 +111,13 @@ class Workload:
             self.keep.extend(ts)
             return [None if t is None else t.data_ptr() for t in ts]
 
-        def norm(rows):
-            x, sc, sh = randn(rows, H), randn(H, std=0.1), randn(H, std=0.1)
-            y, q = empty(rows, H), empty(rows, H, dtype=torch.uint8)
+        def norm(rows, hidden=H, want_y=True):
+            x, sc, sh = randn(rows, hidden), randn(hidden, std=0.1), randn(hidden, std=0.1)
+            y = empty(rows, hidden) if want_y else None
+            q = empty(rows, hidden, dtype=torch.uint8)
             p = P(y, q, x, sc, sh, s0625)
-            return bytes_norm(rows, H), lambda: qe.dit_norm_modulate_fp8(
-                *p, rows, H, 1e-6, stream=st)
+            return bytes_norm(rows, hidden, y=want_y), lambda: qe.dit_norm_modulate_fp8(
+                *p, rows, hidden, 1e-6, stream=st)
 
         def qkv(heads=HEADS, shared_cache=False):
             W = heads * HEAD_DIM
@@ -140,13 +143,14 @@ class Workload:
                 *o, *i3, IMG, 3 * W, *t3, TXT, 3 * W, *w4, *r4, stride, heads, HEAD_DIM,
                 1e-6, 1e-6, stream=st)
 
-        def sr_norm():
+        def sr_norm(want_q=True):
             x, res = randn(IMG, H), randn(IMG, H)
             b, gt = randn(H, std=0.02), randn(H, std=0.1, mean=1.0)
             sc, sh = randn(H, std=0.1), randn(H, std=0.1)
-            r, y, q = empty(IMG, H), empty(IMG, H), empty(IMG, H, dtype=torch.uint8)
-            p = P(r, y, q, x, b, gt, res, sc, sh, s0625)
-            return bytes_sr(IMG, H), lambda: qe.dit_scale_residual_norm_modulate_fp8(
+            r, y = empty(IMG, H), empty(IMG, H)
+            q = empty(IMG, H, dtype=torch.uint8) if want_q else None
+            p = P(r, y, q, x, b, gt, res, sc, sh, s0625 if want_q else None)
+            return bytes_sr(IMG, H, q=want_q), lambda: qe.dit_scale_residual_norm_modulate_fp8(
                 *p, IMG, H, 1e-6, stream=st)
 
         def bma():
@@ -178,6 +182,8 @@ class Workload:
             "cat_fp8": lambda: cat(qe.DIT_QUANT_FP8_E4M3),
             "cat_fp4": lambda: cat(qe.DIT_QUANT_FP4_E2M1),
             "qkv_flux2": lambda: qkv(heads=FLUX_HEADS, shared_cache=True),
+            "norm_flux2_fp8": lambda: norm(FLUX_ROWS, FLUX_A, want_y=False),
+            "sr_norm_bf16": lambda: sr_norm(want_q=False),
         }
         self.launches = []  # (name, compulsory bytes, launch)
         for n in names:
@@ -250,6 +256,7 @@ KERNEL_SOURCES = {
     "norm_img": "norm_modulate.hip", "norm_txt": "norm_modulate.hip", "sr_norm": "norm_modulate.hip",
     "qkv": "qkv_epilogue.hip", "bma": "bias_mul_add.hip", "cat_fp8": "token_cat_quant.hip",
     "cat_fp4": "token_cat_quant.hip", "qkv_flux2": "qkv_epilogue.hip",
+    "norm_flux2_fp8": "norm_modulate.hip", "sr_norm_bf16": "norm_modulate.hip",
 }
 
 

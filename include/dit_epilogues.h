@@ -71,8 +71,12 @@ const char* dit_last_error(void);
  * is rounded to bf16; y = bf16(norm * (1 + scale) + shift); the FP8 output is
  * e4m3(clamp(y * (1 / input_scale), -448, 448)). Both outputs are written.
  *
- *   y      [rows, hidden] bf16, out
- *   q      [rows, hidden] E4M3FN bytes, out
+ *   y      [rows, hidden] bf16, out; NULLABLE: FP8-only output, the bf16 y is
+ *          still formed (q is computed from it) but not written, as the FLUX.2
+ *          variant on the sglang PR 37162 page ("Implementation breakdown"
+ *          item 1) drops the bf16 intermediate
+ *   q      [rows, hidden] E4M3FN bytes, out; NULLABLE: bf16-only output
+ *          (input_scale_dev may then be NULL too). y and q are not both NULL.
  *   x      [rows, hidden] bf16, in
  *   scale, shift  [hidden] bf16, in (broadcast over rows)
  *   input_scale_dev  device fp32 scalar (static FP8 scale; q = y / scale)
@@ -98,7 +102,9 @@ int dit_norm_modulate_fp8(void* y, uint8_t* q, const void* x, const void* scale,
  *   residual_out [rows, hidden] bf16, out:
  *       bf16(residual + gate * xb) with ONE rounding, xb = bf16(x + bias)
  *       (xb = x when bias is NULL)
- *   y, q         as dit_norm_modulate_fp8, computed from residual_out
+ *   y, q         as dit_norm_modulate_fp8 (either may be NULL), computed
+ *                from residual_out; q == NULL is the bf16-only bias + gated
+ *                residual norm of the sglang PR 37116 page
  *   x, residual  [rows, hidden] bf16, in
  *   bias         [hidden] bf16, in, NULLABLE
  *   gate, scale, shift  [hidden] bf16, in

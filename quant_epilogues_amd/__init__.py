@@ -35,35 +35,46 @@ def _scalar_f32(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be a one-element fp32 device tensor")
 
 
+def _outputs(x, want_y, want_q, input_scale):
+    if not (want_y or want_q):
+        raise ValueError("at least one of the bf16 and FP8 outputs must be requested")
+    if want_q:
+        _scalar_f32(input_scale, "input_scale")
+    y = torch.empty_like(x) if want_y else None
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if want_q else None
+    return y, q
+
+
 def norm_modulate_fp8(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
-                      input_scale: torch.Tensor, eps: float = 1e-6):
-    """LayerNorm (no affine) + AdaLN scale/shift + static FP8: returns (y, q)."""
+                      input_scale: torch.Tensor | None, eps: float = 1e-6,
+                      want_y: bool = True, want_q: bool = True):
+    """LayerNorm (no affine) + AdaLN scale/shift + static FP8: returns (y, q);
+    an output not asked for is None (and not written)."""
     for t, n in ((x, "x"), (scale, "scale"), (shift, "shift")):
         _dense_bf16(t, n)
-    _scalar_f32(input_scale, "input_scale")
     hidden = x.shape[-1]
-    y = torch.empty_like(x)
-    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    dit_norm_modulate_fp8(y, q, x, scale, shift, input_scale, x.numel() // hidden, hidden, eps)
+    y, q = _outputs(x, want_y, want_q, input_scale)
+    dit_norm_modulate_fp8(y, q, x, scale, shift, input_scale if want_q else None,
+                          x.numel() // hidden, hidden, eps)
     return y, q
 
 
 def scale_residual_norm_modulate_fp8(x, bias, gate, residual, scale, shift, input_scale,
-                                     eps: float = 1e-6):
+                                     eps: float = 1e-6, want_y: bool = True,
+                                     want_q: bool = True):
     """bias (optional) + gated residual, then norm/modulate/FP8:
-    returns (residual_out, y, q)."""
+    returns (residual_out, y, q); an output not asked for is None."""
     for t, n in ((x, "x"), (gate, "gate"), (residual, "residual"), (scale, "scale"),
                  (shift, "shift")):
         _dense_bf16(t, n)
     if bias is not None:
         _dense_bf16(bias, "bias")
-    _scalar_f32(input_scale, "input_scale")
     hidden = x.shape[-1]
     r = torch.empty_like(x)
-    y = torch.empty_like(x)
-    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    y, q = _outputs(x, want_y, want_q, input_scale)
     dit_scale_residual_norm_modulate_fp8(r, y, q, x, bias, gate, residual, scale, shift,
-                                         input_scale, x.numel() // hidden, hidden, eps)
+                                         input_scale if want_q else None,
+                                         x.numel() // hidden, hidden, eps)
     return r, y, q
 
 

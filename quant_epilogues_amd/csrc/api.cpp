@@ -84,8 +84,9 @@ int dit_norm_modulate_fp8(void* y, uint8_t* q, const void* x, const void* scale,
                           const void* shift, const float* input_scale_dev, int64_t rows,
                           int64_t hidden, float eps, void* stream) {
     const char* fn = "dit_norm_modulate_fp8";
-    if (!y || !q || !x || !scale || !shift || !input_scale_dev)
-        return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);
+    if (!x || !scale || !shift || (!y && !q) || (q && !input_scale_dev))
+        return fail(DIT_ERR_NULL, "%s: a required pointer is NULL (y and q may not both be NULL; "
+                    "q needs input_scale)", fn);
     if (int st = check_norm_shape(fn, rows, hidden)) return st;
     if (!aligned(y, 16) || !aligned(q, 16) || !aligned(x, 16) || !aligned(scale, 16) ||
         !aligned(shift, 16) || !aligned(input_scale_dev, 4))
@@ -111,9 +112,10 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
                                          const void* shift, const float* input_scale_dev,
                                          int64_t rows, int64_t hidden, float eps, void* stream) {
     const char* fn = "dit_scale_residual_norm_modulate_fp8";
-    if (!residual_out || !y || !q || !x || !gate || !residual || !scale || !shift ||
-        !input_scale_dev)
-        return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);
+    if (!residual_out || !x || !gate || !residual || !scale || !shift || (!y && !q) ||
+        (q && !input_scale_dev))
+        return fail(DIT_ERR_NULL, "%s: a required pointer is NULL (y and q may not both be NULL; "
+                    "q needs input_scale)", fn);
     if (int st = check_norm_shape(fn, rows, hidden)) return st;
     if (!aligned(residual_out, 16) || !aligned(y, 16) || !aligned(q, 16) || !aligned(x, 16) ||
         (bias && !aligned(bias, 16)) || !aligned(gate, 16) || !aligned(residual, 16) ||

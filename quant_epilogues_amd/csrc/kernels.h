@@ -16,8 +16,8 @@ constexpr hipError_t kGridTooLarge = hipErrorInvalidConfiguration;
 // LayerNorm + AdaLN modulation + static FP8 (optionally after bias + gated
 // residual). residual == nullptr selects the plain variant.
 struct NormModulateArgs {
-    uint16_t* y;             // [rows, hidden] bf16
-    uint8_t* q;              // [rows, hidden] e4m3
+    uint16_t* y;             // [rows, hidden] bf16, or nullptr: not written
+    uint8_t* q;              // [rows, hidden] e4m3, or nullptr: not computed
     uint16_t* r_out;         // [rows, hidden] bf16 (residual variant only)
     const uint16_t* x;       // [rows, hidden]
     const uint16_t* residual;  // [rows, hidden] or nullptr
@@ -25,7 +25,7 @@ struct NormModulateArgs {
     const uint16_t* gate;    // [hidden] (residual variant only)
     const uint16_t* scale;   // [hidden]
     const uint16_t* shift;   // [hidden]
-    const float* input_scale;  // device scalar
+    const float* input_scale;  // device scalar (read only when q is written)
     int64_t rows;
     int32_t hidden;          // multiple of 8, <= kMaxHidden (one thread per 8 columns)
     float eps;

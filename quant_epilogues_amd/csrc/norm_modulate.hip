@@ -89,7 +89,8 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
         if (MODE != kPlain) rin[k] = ok[k] ? stream_load16(a.residual + base + 8 * c) : (u32x4){0, 0, 0, 0};
     }
 
-    const float inv = 1.0f / *a.input_scale;  // IEEE division
+    const bool want_y = a.y != nullptr, want_q = a.q != nullptr;  // wave-uniform
+    const float inv = want_q ? 1.0f / *a.input_scale : 0.0f;  // IEEE division
 
     // 2. Column vectors to fp32 in LDS, while the streaming loads are in flight.
     if (kLds) {
@@ -203,12 +204,14 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
             yv[i] = bf_lo(yw[i / 2]);
             yv[i + 1] = bf_hi(yw[i / 2]);
         }
-        const uint32_t q0 = pack_e4m3x4(clamp_e4m3(yv[0] * inv), clamp_e4m3(yv[1] * inv),
-                                        clamp_e4m3(yv[2] * inv), clamp_e4m3(yv[3] * inv));
-        const uint32_t q1 = pack_e4m3x4(clamp_e4m3(yv[4] * inv), clamp_e4m3(yv[5] * inv),
-                                        clamp_e4m3(yv[6] * inv), clamp_e4m3(yv[7] * inv));
-        store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
-        store8(a.q + base + 8 * c, (u32x2){q0, q1});
+        if (want_y) store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
+        if (want_q) {  // from the bf16 y, stored or not
+            const uint32_t q0 = pack_e4m3x4(clamp_e4m3(yv[0] * inv), clamp_e4m3(yv[1] * inv),
+                                            clamp_e4m3(yv[2] * inv), clamp_e4m3(yv[3] * inv));
+            const uint32_t q1 = pack_e4m3x4(clamp_e4m3(yv[4] * inv), clamp_e4m3(yv[5] * inv),
+                                            clamp_e4m3(yv[6] * inv), clamp_e4m3(yv[7] * inv));
+            store8(a.q + base + 8 * c, (u32x2){q0, q1});
+        }
     }
 }
 

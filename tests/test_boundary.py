@@ -70,7 +70,7 @@ def _nm(L, **kw):
 
 def test_norm_modulate_refusals(native):
     L = native.lib()
-    assert _nm(L, y=None) == native.DIT_ERR_NULL
+    assert _nm(L, x=None) == native.DIT_ERR_NULL
     assert "NULL" in native.last_error()
     assert _nm(L, rows=-1) == native.DIT_ERR_SHAPE
     assert _nm(L, hidden=0) == native.DIT_ERR_SHAPE
@@ -81,6 +81,11 @@ def test_norm_modulate_refusals(native):
     assert _nm(L, s=FAKE + 2) == native.DIT_ERR_ALIGN
     assert _nm(L, rows=0) == native.DIT_OK  # no-op, no HIP call
     assert native.last_error() == ""
+    # Either output may be left out, not both; q needs the scale.
+    assert _nm(L, y=None, q=None) == native.DIT_ERR_NULL
+    assert _nm(L, s=None) == native.DIT_ERR_NULL
+    assert _nm(L, y=None, rows=0) == native.DIT_OK
+    assert _nm(L, q=None, s=None, rows=0) == native.DIT_OK
 
 
 def test_scale_residual_refusals(native):
@@ -100,6 +105,13 @@ def test_scale_residual_refusals(native):
     bad = list(args)
     bad[11] = 12
     assert f(*bad) == native.DIT_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[1] = bad[2] = None  # neither y nor q
+    assert f(*bad) == native.DIT_ERR_NULL
+    bad = list(args)
+    bad[2] = bad[9] = None  # bf16 only, no scale needed
+    bad[10] = 0
+    assert f(*bad) == native.DIT_OK
 
 
 def _qkv(L, **kw):

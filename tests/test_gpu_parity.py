@@ -141,6 +141,55 @@ def test_scale_residual_norm_modulate_fp8(qe, oracle_mod, e4m3_table, rows, hidd
     print(f"exact: r {er:.6f} y {ey:.6f} q {eq:.6f}")
 
 
+SELECT_CASES = [
+    # (rows, hidden, input_scale, residual variant, with_bias, write y, write q, seed)
+    (4608, 6144, 0.0625, False, False, False, True, 30),  # FLUX.2 LN + modulate, FP8 only
+    (4096, 3072, 0.0625, True, True, True, False, 31),    # Qwen-Image bias + residual norm, bf16 only
+    (4096, 3072, 0.02, True, True, False, True, 32),
+    (127, 3072, 0.0625, False, False, True, False, 33),
+    (17, 1000, 0.5, True, False, False, True, 34),
+]
+
+
+@pytest.mark.parametrize("rows,hidden,input_scale,resid,with_bias,want_y,want_q,seed", SELECT_CASES)
+def test_norm_output_selection(qe, oracle_mod, e4m3_table, rows, hidden, input_scale, resid,
+                               with_bias, want_y, want_q, seed):
+    """One of the two outputs not requested (NULL): the other is unchanged."""
+    _print_case("norm output selection", rows, hidden, input_scale, resid, with_bias, want_y,
+                want_q, seed)
+    y = Guarded((rows, hidden), torch.bfloat16) if want_y else None
+    q = Guarded((rows, hidden), torch.uint8) if want_q else None
+    s = dscalar(input_scale) if want_q else None
+    if resid:
+        inp = synth.scale_residual_inputs(rows, hidden, seed=seed, input_scale=input_scale,
+                                          with_bias=with_bias)
+        r = Guarded((rows, hidden), torch.bfloat16)
+        qe.dit_scale_residual_norm_modulate_fp8(
+            r.t, y and y.t, q and q.t, dev(inp.x), dev(inp.bias), dev(inp.gate),
+            dev(inp.residual), dev(inp.scale), dev(inp.shift), s, rows, hidden, inp.eps)
+        rr, ry, rq, pre = oracle_mod.scale_residual_norm_modulate_fp8(
+            bits(inp.x), None if inp.bias is None else bits(inp.bias), bits(inp.gate),
+            bits(inp.residual), bits(inp.scale), bits(inp.shift), inp.input_scale, inp.eps)
+    else:
+        inp = synth.norm_modulate_inputs(rows, hidden, seed=seed, input_scale=input_scale)
+        qe.dit_norm_modulate_fp8(y and y.t, q and q.t, dev(inp.x), dev(inp.scale),
+                                 dev(inp.shift), s, rows, hidden, inp.eps)
+        ry, rq, pre = oracle_mod.norm_modulate_fp8(bits(inp.x), bits(inp.scale),
+                                                   bits(inp.shift), inp.input_scale, inp.eps)
+    torch.cuda.synchronize()
+    msg = []
+    if resid:
+        r.check("r")
+        msg.append(f"r {check_bf16('residual_out', r.bits(), rr):.6f}")
+    if want_y:
+        y.check("y")
+        msg.append(f"y {check_bf16('y', y.bits(), ry):.6f}")
+    if want_q:
+        q.check("q")
+        msg.append(f"q {check_fp8('q', q.bits(), rq, pre, e4m3_table):.6f}")
+    print("exact: " + " ".join(msg))
+
+
 def test_fp8_split_equals_fused_on_gpu(qe):
     """q of the fused kernel == y re-quantised by the token-cat FP8 path."""
     inp = synth.norm_modulate_inputs(256, 3072, seed=21, input_scale=0.4754464328)
