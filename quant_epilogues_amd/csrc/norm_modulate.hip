@@ -227,11 +227,13 @@ hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Geometries measured on MI355X at hidden 3072 (time per call over
-// back-to-back launches with rotating buffers):
+// Geometries measured on MI355X (time per call over back-to-back launches
+// with rotating buffers), at hidden 3072 unless stated:
 //  - fewer than 1024 rows (latency-bound): six waves per row, two rows per
 //    workgroup, column vectors read from L2;
 //  - plain variant, many rows: two waves per row, four rows per workgroup;
+//    at hidden 6144 (FLUX.2) six waves per row and two rows per workgroup
+//    with both outputs, four waves and one row with the FP8 output only;
 //  - residual variants, many rows: one wave per row, eight rows per workgroup,
 //    column vectors staged in LDS when they fit in 48 KiB.
 template <int MODE>
@@ -242,6 +244,12 @@ hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
             case 1: return launch_geom<MODE, 6, 2, 1, false>(a, stream);
             case 2: return launch_geom<MODE, 6, 2, 2, false>(a, stream);
             default: return launch_geom<MODE, 6, 2, 3, false>(a, stream);  // up to 1152 chunks
+        }
+    }
+    if constexpr (MODE == kPlain) {
+        if (cpr > 384 && cpr <= 768) {
+            return a.y ? launch_geom<MODE, 6, 2, 2, false>(a, stream)
+                       : launch_geom<MODE, 4, 1, 3, false>(a, stream);
         }
     }
     if constexpr (MODE != kPlain) {

@@ -84,6 +84,8 @@ NORM_CASES = [
     (33, 512, 0.0625, 4),
     (17, 1000, 0.0625, 5),    # ragged: 125 chunks, a partial last wave
     (9, 6144, 0.02, 6),       # FLUX.2 width, 12 waves per row
+    (1024, 6144, 0.0625, 9),  # FLUX.2 width, many rows: six waves per row
+    (1030, 4104, 0.5, 10),    # 513 chunks per row: a partial last wave
     (3, 8192, 0.0625, 8),     # widest supported row: 1024 threads
     (5, 8, 0.0625, 7),        # one chunk per row
 ]
@@ -148,6 +150,7 @@ SELECT_CASES = [
     (4096, 3072, 0.02, True, True, False, True, 32),
     (127, 3072, 0.0625, False, False, True, False, 33),
     (17, 1000, 0.5, True, False, False, True, 34),
+    (1030, 4104, 0.0625, False, False, False, True, 35),  # FP8 only, 513 chunks per row
 ]
 
 
