@@ -378,6 +378,8 @@ def main():
                     help="print the source hash of every launch's kernel and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the kernels timed beside the step (FLUX.2 QKV, output selections)")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only, no per-kernel timing (for counter runs)")
     ap.add_argument("--blocks", type=int, default=0,
@@ -421,7 +423,7 @@ def main():
                          "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                          "us_in_step": round(1e3 * marg, 3), "rotation_sets": t["sets"]}
     extra = {}
-    if not args.only:
+    if not args.only and not args.no_extra:
         ex = Workload(torch, qe, seed=0, names=Workload.EXTRA)
         _, ext = kernel_timings(torch, qe, ex, args.steps, in_step=False)
         for name, nbytes, _ in ex.launches:
