@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
             "oracle_bias_mul_add": (None, [P, P, P, P, P, I64, I64]),
             "oracle_token_cat_fp8": (None, [P, P, P, I64, P, I64, I64, F]),
             "oracle_token_cat_fp4": (None, [P, P, P, P, P, I64, P, I64, I64, F]),
+            "oracle_norm_modulate_fp4": (None, [P, P, P, P, P, P, P, P, F, I64, I64, F]),
+            "oracle_scale_residual_norm_modulate_fp4":
+                (None, [P, P, P, P, P, P, P, P, P, P, P, P, F, I64, I64, F]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -274,3 +277,37 @@ def token_cat_fp4(a, b, g: float):
     lib().oracle_token_cat_fp4(_ptr(packed), _ptr(scales), _ptr(s_pre), _ptr(pre), _ptr(a),
                                a.shape[1], _ptr(b), b.shape[1], rows, g)
     return packed, scales, s_pre, pre
+
+
+def _fp4_outputs(rows, hidden):
+    rows_pad = (rows + 127) // 128 * 128
+    return (np.empty((rows, hidden // 2), np.uint8), np.empty((rows_pad, hidden // 16), np.uint8),
+            np.empty((rows, hidden // 16), np.float32), np.empty((rows, hidden), np.float32))
+
+
+def norm_modulate_fp4(x, scale, shift, g: float, eps: float):
+    """LayerNorm + modulation, NVFP4 output. Returns (y bf16 bits, packed uint8
+    [rows, hidden/2], scales uint8 [round_up(rows,128), hidden/16], s_pre, pre)."""
+    x, scale, shift = _u16(x), _u16(scale), _u16(shift)
+    rows, hidden = x.shape
+    y = np.empty_like(x)
+    packed, scales, s_pre, pre = _fp4_outputs(rows, hidden)
+    lib().oracle_norm_modulate_fp4(_ptr(y), _ptr(packed), _ptr(scales), _ptr(s_pre), _ptr(pre),
+                                   _ptr(x), _ptr(scale), _ptr(shift), g, rows, hidden, eps)
+    return y, packed, scales, s_pre, pre
+
+
+def scale_residual_norm_modulate_fp4(x, bias, gate, residual, scale, shift, g: float,
+                                     eps: float):
+    """bias + gated residual, LayerNorm + modulation, NVFP4 output. Returns
+    (residual_out, y, packed, scales, s_pre, pre)."""
+    x, gate, residual, scale, shift = map(_u16, (x, gate, residual, scale, shift))
+    bias = None if bias is None else _u16(bias)
+    rows, hidden = x.shape
+    r = np.empty_like(x)
+    y = np.empty_like(x)
+    packed, scales, s_pre, pre = _fp4_outputs(rows, hidden)
+    lib().oracle_scale_residual_norm_modulate_fp4(
+        _ptr(r), _ptr(y), _ptr(packed), _ptr(scales), _ptr(s_pre), _ptr(pre), _ptr(x),
+        _ptr(bias), _ptr(gate), _ptr(residual), _ptr(scale), _ptr(shift), g, rows, hidden, eps)
+    return r, y, packed, scales, s_pre, pre

@@ -226,13 +226,9 @@ float oracle_rms_inverse(const uint16_t* v, int64_t n, float eps) {
 
 /* One row, following the kQuantizeFp8 loop of the norm_scale_shift excerpt
  * ("Key source snippets"): norm = bf16((v - mean) * factor); y = bf16(norm *
- * (1 + scale) + shift); q = e4m3(clamp(y * (1/input_scale), +-448)). The
- * reciprocal is IEEE binary32 division (the page's NVIDIA-specific reciprocal
- * instruction is not reproduced). */
-static void norm_modulate_fp8_row(uint16_t* y, uint8_t* q, float* q_pre,
-                                  const uint16_t* v, const uint16_t* scale,
-                                  const uint16_t* shift, float inv,
-                                  int64_t hidden, float eps) {
+ * (1 + scale) + shift). */
+static void norm_modulate_row(uint16_t* y, const uint16_t* v, const uint16_t* scale,
+                              const uint16_t* shift, int64_t hidden, float eps) {
     float mean, factor;
     oracle_layernorm_stats(v, hidden, eps, &mean, &factor);
     for (int64_t j = 0; j < hidden; ++j) {
@@ -241,13 +237,29 @@ static void norm_modulate_fp8_row(uint16_t* y, uint8_t* q, float* q_pre,
         const float norm = bf(oracle_bf16_from_f32(t));
         const float one_plus_scale = 1.0f + bf(scale[j]);
         const float modulated = fmaf(norm, one_plus_scale, bf(shift[j]));
-        const uint16_t yb = oracle_bf16_from_f32(modulated);
-        y[j] = yb;
-        const float scaled = bf(yb) * inv;
+        y[j] = oracle_bf16_from_f32(modulated);
+    }
+}
+
+/* The same excerpt's FP8 step on one row of y: q = e4m3(clamp(y * (1 /
+ * input_scale), +-448)). The reciprocal is IEEE binary32 division (the page's
+ * NVIDIA-specific reciprocal instruction is not reproduced). */
+static void fp8_quantize_row(uint8_t* q, float* q_pre, const uint16_t* y, float inv,
+                             int64_t hidden) {
+    for (int64_t j = 0; j < hidden; ++j) {
+        const float scaled = bf(y[j]) * inv;
         const float clamped = fminf(fmaxf(scaled, -448.0f), 448.0f);
         q[j] = oracle_e4m3_encode(clamped);
         if (q_pre) q_pre[j] = clamped;
     }
+}
+
+static void norm_modulate_fp8_row(uint16_t* y, uint8_t* q, float* q_pre,
+                                  const uint16_t* v, const uint16_t* scale,
+                                  const uint16_t* shift, float inv,
+                                  int64_t hidden, float eps) {
+    norm_modulate_row(y, v, scale, shift, hidden, eps);
+    fp8_quantize_row(q, q_pre, y, inv, hidden);
 }
 
 void oracle_norm_modulate_fp8(uint16_t* y, uint8_t* q, float* q_pre,
@@ -270,6 +282,16 @@ void oracle_norm_modulate_fp8(uint16_t* y, uint8_t* q, float* q_pre,
  * rounded ONCE to bf16, the same single-rounding rule the bias_mul_add
  * excerpt states for its gated multiply-add. gate * xb is exact in binary64
  * (8 x 8 significant bits). */
+static void gated_residual_row(uint16_t* rr, const uint16_t* xr, const uint16_t* bias,
+                               const uint16_t* gate, const uint16_t* resr, int64_t hidden) {
+    for (int64_t j = 0; j < hidden; ++j) {
+        float xb = bf(xr[j]);
+        if (bias) xb = bf(oracle_bf16_from_f32(xb + bf(bias[j])));
+        const double product = (double)bf(gate[j]) * (double)xb;
+        rr[j] = oracle_bf16_of_exact_sum(product, (double)bf(resr[j]));
+    }
+}
+
 void oracle_scale_residual_norm_modulate_fp8(
     uint16_t* r_out, uint16_t* y, uint8_t* q, float* q_pre,
     const uint16_t* x, const uint16_t* bias, const uint16_t* gate,
@@ -277,15 +299,8 @@ void oracle_scale_residual_norm_modulate_fp8(
     float input_scale, int64_t rows, int64_t hidden, float eps) {
     const float inv = 1.0f / input_scale;
     for (int64_t r = 0; r < rows; ++r) {
-        const uint16_t* xr = x + r * hidden;
-        const uint16_t* resr = residual + r * hidden;
         uint16_t* rr = r_out + r * hidden;
-        for (int64_t j = 0; j < hidden; ++j) {
-            float xb = bf(xr[j]);
-            if (bias) xb = bf(oracle_bf16_from_f32(xb + bf(bias[j])));
-            const double product = (double)bf(gate[j]) * (double)xb;
-            rr[j] = oracle_bf16_of_exact_sum(product, (double)bf(resr[j]));
-        }
+        gated_residual_row(rr, x + r * hidden, bias, gate, residual + r * hidden, hidden);
         norm_modulate_fp8_row(y + r * hidden, q + r * hidden,
                               q_pre ? q_pre + r * hidden : NULL, rr, scale,
                               shift, inv, hidden, eps);
@@ -429,6 +444,28 @@ void oracle_token_cat_fp8(uint8_t* out, float* pre, const uint16_t* a,
  * Pinned by closed forms (exactly representable groups, zero and saturating
  * groups, the dequantisation error bound); parity with the page's third-party
  * primitive itself is unpinned, since the page shows none of its outputs. */
+static void fp4_quantize_row(uint8_t* packed, uint8_t* scales, float* s_pre, float* pre,
+                             const uint16_t* row, int64_t cols, float g) {
+    for (int64_t gi = 0; gi < cols / 16; ++gi) {
+        const uint16_t* grp = row + gi * 16;
+        float amax = 0.0f;
+        for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(bf(grp[k])));
+        const float sp = (amax / 6.0f) * g;
+        const uint8_t s8 = oracle_e4m3_encode(fminf(sp, 448.0f));
+        const float kscale = (s8 == 0) ? 0.0f : g / (float)oracle_e4m3_decode(s8);
+        uint8_t codes[16];
+        for (int k = 0; k < 16; ++k) {
+            const float t = bf(grp[k]) * kscale;
+            codes[k] = (s8 == 0) ? 0 : oracle_e2m1_encode(t);
+            if (pre) pre[gi * 16 + k] = t;
+        }
+        for (int k = 0; k < 8; ++k)
+            packed[gi * 8 + k] = (uint8_t)(codes[2 * k] | (codes[2 * k + 1] << 4));
+        scales[gi] = s8;
+        if (s_pre) s_pre[gi] = sp;
+    }
+}
+
 void oracle_token_cat_fp4(uint8_t* packed, uint8_t* scales, float* s_pre,
                           float* pre, const uint16_t* a, int64_t a_cols,
                           const uint16_t* b, int64_t b_cols, int64_t rows,
@@ -440,25 +477,47 @@ void oracle_token_cat_fp4(uint8_t* packed, uint8_t* scales, float* s_pre,
     uint16_t* row = (uint16_t*)malloc((size_t)(cols ? cols : 1) * sizeof(uint16_t));
     for (int64_t r = 0; r < rows; ++r) {
         cat_row(row, a, a_cols, b, b_cols, r);
-        for (int64_t gi = 0; gi < groups; ++gi) {
-            const uint16_t* grp = row + gi * 16;
-            float amax = 0.0f;
-            for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(bf(grp[k])));
-            const float sp = (amax / 6.0f) * g;
-            const uint8_t s8 = oracle_e4m3_encode(fminf(sp, 448.0f));
-            const float kscale = (s8 == 0) ? 0.0f : g / (float)oracle_e4m3_decode(s8);
-            uint8_t codes[16];
-            for (int k = 0; k < 16; ++k) {
-                const float t = bf(grp[k]) * kscale;
-                codes[k] = (s8 == 0) ? 0 : oracle_e2m1_encode(t);
-                if (pre) pre[r * cols + gi * 16 + k] = t;
-            }
-            for (int k = 0; k < 8; ++k)
-                packed[r * (cols / 2) + gi * 8 + k] =
-                    (uint8_t)(codes[2 * k] | (codes[2 * k + 1] << 4));
-            scales[r * groups + gi] = s8;
-            if (s_pre) s_pre[r * groups + gi] = sp;
-        }
+        fp4_quantize_row(packed + r * (cols / 2), scales + r * groups,
+                         s_pre ? s_pre + r * groups : NULL, pre ? pre + r * cols : NULL,
+                         row, cols, g);
     }
     free(row);
+}
+
+/* ======================================================================== */
+/* NVFP4 output on the LayerNorm path                                       */
+/* ======================================================================== */
+
+/* The (residual-)norm variants with NVFP4 instead of FP8 output. The pages
+ * only name this fusion (the Qwen-Image residual norm + NVFP4 PR, listed
+ * among the related PRs of the sglang PR 37123 and PR 37162 pages). Reading:
+ * the bf16 y of the FP8 variants, quantised exactly as the token-cat FP4
+ * output of the sglang PR 37141 page (16-element groups, E4M3 scale from the
+ * global inverse scale g, row-major scales, pad rows to a multiple of 128
+ * with zero scales). */
+void oracle_norm_modulate_fp4(uint16_t* y, uint8_t* packed, uint8_t* scales,
+                              float* s_pre, float* pre, const uint16_t* x,
+                              const uint16_t* scale, const uint16_t* shift,
+                              float g, int64_t rows, int64_t hidden, float eps) {
+    const int64_t groups = hidden / 16;
+    const int64_t rows_padded = ((rows + 127) / 128) * 128;
+    memset(scales, 0, (size_t)(rows_padded * groups));
+    for (int64_t r = 0; r < rows; ++r) {
+        norm_modulate_row(y + r * hidden, x + r * hidden, scale, shift, hidden, eps);
+        fp4_quantize_row(packed + r * (hidden / 2), scales + r * groups,
+                         s_pre ? s_pre + r * groups : NULL, pre ? pre + r * hidden : NULL,
+                         y + r * hidden, hidden, g);
+    }
+}
+
+void oracle_scale_residual_norm_modulate_fp4(
+    uint16_t* r_out, uint16_t* y, uint8_t* packed, uint8_t* scales, float* s_pre,
+    float* pre, const uint16_t* x, const uint16_t* bias, const uint16_t* gate,
+    const uint16_t* residual, const uint16_t* scale, const uint16_t* shift,
+    float g, int64_t rows, int64_t hidden, float eps) {
+    for (int64_t r = 0; r < rows; ++r)
+        gated_residual_row(r_out + r * hidden, x + r * hidden, bias, gate,
+                           residual + r * hidden, hidden);
+    oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, r_out, scale, shift, g, rows,
+                             hidden, eps);
 }

@@ -116,6 +116,20 @@ void oracle_token_cat_fp4(uint8_t* packed, uint8_t* scales, float* s_pre,
                           const uint16_t* b, int64_t b_cols, int64_t rows,
                           float g);
 
+/* NVFP4 output on the LayerNorm path: y as oracle_norm_modulate_fp8, then
+ * 16-element-group FP4 of the bf16 y (as oracle_token_cat_fp4). packed is
+ * [rows, hidden/2], scales [round_up(rows, 128), hidden/16] (pad rows 0),
+ * s_pre [rows, hidden/16] and pre [rows, hidden] optional. hidden % 16 == 0. */
+void oracle_norm_modulate_fp4(uint16_t* y, uint8_t* packed, uint8_t* scales,
+                              float* s_pre, float* pre, const uint16_t* x,
+                              const uint16_t* scale, const uint16_t* shift,
+                              float g, int64_t rows, int64_t hidden, float eps);
+void oracle_scale_residual_norm_modulate_fp4(
+    uint16_t* r_out, uint16_t* y, uint8_t* packed, uint8_t* scales, float* s_pre,
+    float* pre, const uint16_t* x, const uint16_t* bias, const uint16_t* gate,
+    const uint16_t* residual, const uint16_t* scale, const uint16_t* shift,
+    float g, int64_t rows, int64_t hidden, float eps);
+
 #ifdef __cplusplus
 }
 #endif

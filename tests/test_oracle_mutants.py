@@ -23,7 +23,7 @@ ORACLE_C = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_TESTS = [os.path.join(ROOT, "tests", "test_oracle_codecs.py"),
              os.path.join(ROOT, "tests", "test_oracle_ops.py")]
 
-# name -> [(exact text in oracle.c, replacement), ...]
+# name -> [(exact text in oracle.c, replacement[, occurrences]), ...]
 MUTANTS = {
     "bf16 ties round away from zero": [
         ("r = (bf16_bits_of_representable(lo) & 1u) ? hi : lo; /* tie: even */", "r = hi;")],
@@ -47,7 +47,7 @@ MUTANTS = {
     "modulation uses scale instead of 1 + scale": [
         ("const float one_plus_scale = 1.0f + bf(scale[j]);", "const float one_plus_scale = bf(scale[j]);")],
     "FP8 multiplies by the scale instead of its reciprocal": [
-        ("const float scaled = bf(yb) * inv;", "const float scaled = bf(yb) / inv;")],
+        ("const float scaled = bf(y[j]) * inv;", "const float scaled = bf(y[j]) / inv;")],
     "gated residual: bias add not rounded to bf16": [
         ("if (bias) xb = bf(oracle_bf16_from_f32(xb + bf(bias[j])));", "if (bias) xb = xb + bf(bias[j]);")],
     "gated residual rounded twice": [
@@ -87,13 +87,21 @@ MUTANTS = {
     "FP4 nibbles swapped": [
         ("(uint8_t)(codes[2 * k] | (codes[2 * k + 1] << 4));", "(uint8_t)(codes[2 * k + 1] | (codes[2 * k] << 4));")],
     "FP4 pad-row scales not zero": [
-        ("memset(scales, 0, (size_t)(rows_padded * groups));", "memset(scales, 0x38, (size_t)(rows_padded * groups));")],
+        ("memset(scales, 0, (size_t)(rows_padded * groups));", "memset(scales, 0x38, (size_t)(rows_padded * groups));", 2)],
+    "norm FP4 quantises the input row instead of y": [
+        ("y + r * hidden, hidden, g);", "x + r * hidden, hidden, g);")],
+    "residual norm FP4 normalises x instead of the new residual": [
+        ("oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, r_out, scale, shift, g, rows,",
+         "oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, x, scale, shift, g, rows,")],
 }
 
 
 def _mutate(source, edits):
-    for old, new in edits:
-        assert source.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    """Applies (old, new) or (old, new, count) edits; `old` must occur exactly
+    once (or `count` times, all replaced)."""
+    for old, new, *count in edits:
+        n = count[0] if count else 1
+        assert source.count(old) == n, f"mutation anchor not found exactly {n} times: {old!r}"
         source = source.replace(old, new)
     return source
 

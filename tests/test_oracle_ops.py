@@ -470,3 +470,51 @@ def test_fp4_dequantisation_error_bound_and_branch_split(oracle_mod):
     pb, sb, _, _ = oracle_mod.token_cat_fp4(m_bits, np.zeros((9, 0), np.uint16), inp.fp4_g)
     assert np.array_equal(packed, np.concatenate([pa, pb], axis=1))
     assert np.array_equal(scales, np.concatenate([sa, sb], axis=1))
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 output on the LayerNorm path
+# ---------------------------------------------------------------------------
+
+def test_norm_fp4_closed_form_alternating_rows(oracle_mod):
+    """Rows alternating +a, -a (a >= 1) normalise to exactly +-1, so with scale =
+    shift = 0 and g = 6 every group has amax 1, s_pre = 1 (scale code 0x38),
+    element scale 6 and codes +-6: each byte is 0xF7 (+6 low, -6 high)."""
+    rows, hidden = 5, 256
+    a = np.array([1.0, 1.5, 2.0, 3.0, 96.0], np.float32)
+    x = np.tile(np.array([1.0, -1.0], np.float32), hidden // 2)[None, :] * a[:, None]
+    zeros = np.zeros(hidden, np.uint16)
+    y, packed, scales, s_pre, _ = oracle_mod.norm_modulate_fp4(bfbits(x).reshape(rows, hidden),
+                                                               zeros, zeros, 6.0, 1e-6)
+    assert np.array_equal(bf2f(y).reshape(rows, hidden), np.sign(x))
+    assert np.all(packed == 0xF7)
+    assert np.all(s_pre == 1.0) and np.all(scales[:rows] == 0x38) and np.all(scales[rows:] == 0)
+
+
+@pytest.mark.parametrize("g", [1.0, 448.0, 1e4])
+def test_norm_fp4_is_the_fp4_of_the_bf16_y(oracle_mod, g):
+    """Fused == split: y equals the FP8 variant's y, and the NVFP4 outputs equal
+    the token-cat FP4 quantiser applied to that y."""
+    inp = synth.norm_modulate_inputs(rows=9, hidden=512, seed=12)
+    b = synth.bf16_bits
+    y, packed, scales, s_pre, pre = oracle_mod.norm_modulate_fp4(
+        b(inp.x), b(inp.scale), b(inp.shift), g, inp.eps)
+    y8, _, _ = oracle_mod.norm_modulate_fp8(b(inp.x), b(inp.scale), b(inp.shift), 0.0625, inp.eps)
+    assert np.array_equal(y, y8)
+    p2, s2, sp2, pre2 = oracle_mod.token_cat_fp4(y, np.zeros((9, 0), np.uint16), g)
+    assert np.array_equal(packed, p2) and np.array_equal(scales, s2)
+    assert np.array_equal(s_pre, sp2) and np.array_equal(pre, pre2)
+
+
+def test_scale_residual_fp4_is_the_norm_fp4_of_residual_out(oracle_mod):
+    inp = synth.scale_residual_inputs(rows=7, hidden=1024, seed=13)
+    b = synth.bf16_bits
+    r, y, packed, scales, _, _ = oracle_mod.scale_residual_norm_modulate_fp4(
+        b(inp.x), b(inp.bias), b(inp.gate), b(inp.residual), b(inp.scale), b(inp.shift), 448.0,
+        inp.eps)
+    r8, _, _, _ = oracle_mod.scale_residual_norm_modulate_fp8(
+        b(inp.x), b(inp.bias), b(inp.gate), b(inp.residual), b(inp.scale), b(inp.shift), 0.0625,
+        inp.eps)
+    assert np.array_equal(r, r8)
+    y2, p2, s2, _, _ = oracle_mod.norm_modulate_fp4(r, b(inp.scale), b(inp.shift), 448.0, inp.eps)
+    assert np.array_equal(y, y2) and np.array_equal(packed, p2) and np.array_equal(scales, s2)
