@@ -58,6 +58,12 @@ def bytes_qkv(n_tok, heads, head_dim):
     return 12 * n_tok * heads * head_dim + 2 * 4 * n_tok * (head_dim // 2) + 4 * 2 * head_dim
 
 
+def bytes_sr_fp4(rows, hidden, bias=True, y=True):
+    rows_pad = (rows + 127) // 128 * 128
+    return ((6 + 2 * y) * rows * hidden + rows * hidden // 2 + rows_pad * (hidden // 16)
+            + (8 if bias else 6) * hidden + 4)
+
+
 def bytes_bma(rows, hidden, bias=True):
     return 6 * rows * hidden + (4 if bias else 2) * hidden
 
@@ -79,8 +85,9 @@ class Workload:
     # Timed beside the step, not in it: the FLUX.2 shape of the QKV epilogue
     # (4096 image + 512 text tokens, 48 heads, one shared [cos | sin] cache),
     # the FP8-only LayerNorm + modulation at the FLUX.2 shape (4608 x 6144, no
-    # bf16 output) and the bf16-only bias + gated-residual norm (no FP8).
-    EXTRA = ("qkv_flux2", "norm_flux2_fp8", "sr_norm_bf16")
+    # bf16 output), the bf16-only bias + gated-residual norm (no FP8) and the
+    # same norm with NVFP4 output (4096 x 3072, g = 448).
+    EXTRA = ("qkv_flux2", "norm_flux2_fp8", "sr_norm_bf16", "sr_norm_fp4")
 
     def __init__(self, torch, qe, seed=0, names=ALL):
         import numpy as np
@@ -153,6 +160,17 @@ class Workload:
             return bytes_sr(IMG, H, q=want_q), lambda: qe.dit_scale_residual_norm_modulate_fp8(
                 *p, IMG, H, 1e-6, stream=st)
 
+        def sr_norm_fp4():
+            x, res = randn(IMG, H), randn(IMG, H)
+            b, gt = randn(H, std=0.02), randn(H, std=0.1, mean=1.0)
+            sc, sh = randn(H, std=0.1), randn(H, std=0.1)
+            r, y = empty(IMG, H), empty(IMG, H)
+            packed = empty(IMG, H // 2, dtype=torch.uint8)
+            scales = empty((IMG + 127) // 128 * 128, H // 16, dtype=torch.uint8)
+            p = P(r, y, packed, scales, x, b, gt, res, sc, sh, scalar(448.0))
+            return bytes_sr_fp4(IMG, H), lambda: qe.dit_scale_residual_norm_modulate_fp4(
+                *p, IMG, H, 1e-6, stream=st)
+
         def bma():
             R = IMG + TXT
             x, res = randn(R, H), randn(R, H)
@@ -184,6 +202,7 @@ class Workload:
             "qkv_flux2": lambda: qkv(heads=FLUX_HEADS, shared_cache=True),
             "norm_flux2_fp8": lambda: norm(FLUX_ROWS, FLUX_A, want_y=False),
             "sr_norm_bf16": lambda: sr_norm(want_q=False),
+            "sr_norm_fp4": sr_norm_fp4,
         }
         self.launches = []  # (name, compulsory bytes, launch)
         for n in names:
@@ -257,6 +276,7 @@ KERNEL_SOURCES = {
     "qkv": "qkv_epilogue.hip", "bma": "bias_mul_add.hip", "cat_fp8": "token_cat_quant.hip",
     "cat_fp4": "token_cat_quant.hip", "qkv_flux2": "qkv_epilogue.hip",
     "norm_flux2_fp8": "norm_modulate.hip", "sr_norm_bf16": "norm_modulate.hip",
+    "sr_norm_fp4": "norm_modulate.hip",
 }
 
 

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 2
+#define DIT_ABI_VERSION 3
 
 typedef enum dit_status {
     DIT_OK = 0,
@@ -119,6 +119,48 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
                                          const float* input_scale_dev,
                                          int64_t rows, int64_t hidden, float eps,
                                          void* stream);
+
+/*
+ * LayerNorm + AdaLN modulation with NVFP4 output: the bf16 y of
+ * dit_norm_modulate_fp8, quantised in 16-element groups exactly as the FP4
+ * output of dit_token_cat_quant (E2M1 codes, one E4M3 scale per group from
+ * the global inverse scale, row-major scales, zero scales on pad rows).
+ *
+ * Defined by: the Qwen-Image residual-norm + NVFP4 fusion that the sglang
+ * PR 37123 and PR 37162 pages list among their related PRs (named only), read
+ * as the composition of the LayerNorm path (sglang PR 37156 page) with the
+ * group FP4 quantisation of the sglang PR 37141 page ("Implementation
+ * breakdown" item 1).
+ *
+ *   y       [rows, hidden] bf16, out; NULLABLE (then only the FP4 output)
+ *   packed  [rows, hidden / 2] bytes, out; element 2k in the low nibble
+ *   scales  [round_up(rows, 128), hidden / 16] E4M3 bytes, out, row-major;
+ *           rows [rows, round_up(rows, 128)) are written as 0x00
+ *   x, scale, shift, eps  as dit_norm_modulate_fp8
+ *   global_scale_dev  device fp32 scalar g: group scale e4m3(amax / 6 * g),
+ *           element code e2m1(y * g / scale)
+ *
+ * hidden must be a multiple of 16 and at most 8192 (else DIT_ERR_UNSUPPORTED).
+ * scales needs no alignment; the other tensors 16 bytes.
+ */
+int dit_norm_modulate_fp4(void* y, uint8_t* packed, uint8_t* scales, const void* x,
+                          const void* scale, const void* shift, const float* global_scale_dev,
+                          int64_t rows, int64_t hidden, float eps, void* stream);
+
+/*
+ * Optional input bias + gated residual, then the same LayerNorm + modulation
+ * with NVFP4 output (residual_out, y and FP4 as above and as
+ * dit_scale_residual_norm_modulate_fp8).
+ *
+ * Defined by: the same related-PR fusion, composed with the gated residual
+ * of the sglang PR 37156 and PR 37116 pages.
+ */
+int dit_scale_residual_norm_modulate_fp4(void* residual_out, void* y, uint8_t* packed,
+                                         uint8_t* scales, const void* x, const void* bias,
+                                         const void* gate, const void* residual,
+                                         const void* scale, const void* shift,
+                                         const float* global_scale_dev, int64_t rows,
+                                         int64_t hidden, float eps, void* stream);
 
 /*
  * QKV epilogue: per-head RMSNorm of Q and K, interleaved RoPE, V copy, and the

@@ -20,7 +20,8 @@ import torch
 from ._native import (  # noqa: F401
     DIT_ERR_ALIGN, DIT_ERR_HIP, DIT_ERR_NULL, DIT_ERR_SHAPE, DIT_ERR_UNSUPPORTED, DIT_OK,
     DIT_QUANT_FP4_E2M1, DIT_QUANT_FP8_E4M3, LIB_PATH, DitError, dit_bias_mul_add,
-    dit_norm_modulate_fp8, dit_qkv_epilogue, dit_scale_residual_norm_modulate_fp8,
+    dit_norm_modulate_fp4, dit_norm_modulate_fp8, dit_qkv_epilogue,
+    dit_scale_residual_norm_modulate_fp4, dit_scale_residual_norm_modulate_fp8,
     dit_token_cat_quant, header_symbols, last_error, lib, status_string,
 )
 
@@ -76,6 +77,48 @@ def scale_residual_norm_modulate_fp8(x, bias, gate, residual, scale, shift, inpu
                                          input_scale if want_q else None,
                                          x.numel() // hidden, hidden, eps)
     return r, y, q
+
+
+def _fp4_outputs(x):
+    rows, hidden = x.numel() // x.shape[-1], x.shape[-1]
+    packed = torch.empty((rows, hidden // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(((rows + 127) // 128 * 128, hidden // 16), dtype=torch.uint8,
+                         device=x.device)
+    return packed, scales
+
+
+def norm_modulate_fp4(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                      global_scale: torch.Tensor, eps: float = 1e-6, want_y: bool = True):
+    """LayerNorm (no affine) + AdaLN scale/shift + 16-element-group FP4: returns
+    (y or None, packed [rows, hidden/2], scales [round_up(rows,128), hidden/16])."""
+    for t, n in ((x, "x"), (scale, "scale"), (shift, "shift")):
+        _dense_bf16(t, n)
+    _scalar_f32(global_scale, "global_scale")
+    hidden = x.shape[-1]
+    y = torch.empty_like(x) if want_y else None
+    packed, scales = _fp4_outputs(x)
+    dit_norm_modulate_fp4(y, packed, scales, x, scale, shift, global_scale, x.numel() // hidden,
+                          hidden, eps)
+    return y, packed, scales
+
+
+def scale_residual_norm_modulate_fp4(x, bias, gate, residual, scale, shift, global_scale,
+                                     eps: float = 1e-6, want_y: bool = True):
+    """bias (optional) + gated residual, then norm/modulate/FP4: returns
+    (residual_out, y or None, packed, scales)."""
+    for t, n in ((x, "x"), (gate, "gate"), (residual, "residual"), (scale, "scale"),
+                 (shift, "shift")):
+        _dense_bf16(t, n)
+    if bias is not None:
+        _dense_bf16(bias, "bias")
+    _scalar_f32(global_scale, "global_scale")
+    hidden = x.shape[-1]
+    r = torch.empty_like(x)
+    y = torch.empty_like(x) if want_y else None
+    packed, scales = _fp4_outputs(x)
+    dit_scale_residual_norm_modulate_fp4(r, y, packed, scales, x, bias, gate, residual, scale,
+                                         shift, global_scale, x.numel() // hidden, hidden, eps)
+    return r, y, packed, scales
 
 
 def _row_view(t: torch.Tensor, width: int, name: str) -> int:

@@ -41,6 +41,9 @@ _SIGNATURES = {
     "dit_qkv_epilogue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _I64,
                                         _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32,
                                         _F, _F, _P]),
+    "dit_norm_modulate_fp4": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
+    "dit_scale_residual_norm_modulate_fp4":
+        (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
     "dit_bias_mul_add": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _P]),
     "dit_token_cat_quant": (ctypes.c_int, [_I32, _P, _P, _P, _I64, _P, _I64, _I64, _P, _P]),
 }
@@ -137,6 +140,22 @@ def dit_qkv_epilogue(joint_q, joint_k, joint_v, img_q, img_k, img_v, img_rows, i
         txt_row_stride, _ptr(img_q_w), _ptr(img_k_w), _ptr(txt_q_w), _ptr(txt_k_w),
         _ptr(img_cos), _ptr(img_sin), _ptr(txt_cos), _ptr(txt_sin), rope_row_stride, heads,
         head_dim, img_eps, txt_eps, _stream(stream, joint_q)))
+
+
+def dit_norm_modulate_fp4(y, packed, scales, x, scale, shift, global_scale_dev, rows, hidden,
+                          eps, stream=None) -> None:
+    _check(lib().dit_norm_modulate_fp4(
+        _ptr(y), _ptr(packed), _ptr(scales), _ptr(x), _ptr(scale), _ptr(shift),
+        _ptr(global_scale_dev), rows, hidden, eps, _stream(stream, x)))
+
+
+def dit_scale_residual_norm_modulate_fp4(residual_out, y, packed, scales, x, bias, gate,
+                                         residual, scale, shift, global_scale_dev, rows, hidden,
+                                         eps, stream=None) -> None:
+    _check(lib().dit_scale_residual_norm_modulate_fp4(
+        _ptr(residual_out), _ptr(y), _ptr(packed), _ptr(scales), _ptr(x), _ptr(bias), _ptr(gate),
+        _ptr(residual), _ptr(scale), _ptr(shift), _ptr(global_scale_dev), rows, hidden, eps,
+        _stream(stream, x)))
 
 
 def dit_bias_mul_add(y, x, bias, gate, residual, rows, hidden, stream=None) -> None:

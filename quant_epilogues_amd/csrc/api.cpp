@@ -140,6 +140,65 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
     return launched(dit::launch_norm_modulate_fp8(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+static int launch_norm_fp4(const char* fn, void* residual_out, void* y, uint8_t* packed,
+                           uint8_t* scales, const void* x, const void* bias, const void* gate,
+                           const void* residual, const void* scale, const void* shift,
+                           const float* g_dev, int64_t rows, int64_t hidden, float eps,
+                           void* stream) {
+    if (int st = check_norm_shape(fn, rows, hidden)) return st;
+    if (hidden % 16 != 0)
+        return fail(DIT_ERR_UNSUPPORTED, "%s: hidden (%lld) must be a multiple of 16 (FP4 groups)",
+                    fn, (long long)hidden);
+    if (!aligned(y, 16) || !aligned(packed, 16) || !aligned(x, 16) || (bias && !aligned(bias, 16)) ||
+        !aligned(gate, 16) || !aligned(residual, 16) || !aligned(residual_out, 16) ||
+        !aligned(scale, 16) || !aligned(shift, 16) || !aligned(g_dev, 4))
+        return fail(DIT_ERR_ALIGN, "%s: tensors must be 16-byte aligned (scales: any; g 4-byte)", fn);
+    if (rows == 0) return ok();
+    dit::NormModulateArgs a{};
+    a.y = static_cast<uint16_t*>(y);
+    a.q = nullptr;
+    a.r_out = static_cast<uint16_t*>(residual_out);
+    a.x = static_cast<const uint16_t*>(x);
+    a.residual = static_cast<const uint16_t*>(residual);
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.gate = static_cast<const uint16_t*>(gate);
+    a.scale = static_cast<const uint16_t*>(scale);
+    a.shift = static_cast<const uint16_t*>(shift);
+    a.input_scale = g_dev;
+    a.fp4 = packed;
+    a.fp4_scales = scales;
+    a.fp4_rows_padded = (rows + 127) / 128 * 128;
+    a.rows = rows;
+    a.hidden = (int32_t)hidden;
+    a.eps = eps;
+    clear_stale_hip_error();
+    return launched(dit::launch_norm_modulate_fp8(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int dit_norm_modulate_fp4(void* y, uint8_t* packed, uint8_t* scales, const void* x,
+                          const void* scale, const void* shift, const float* global_scale_dev,
+                          int64_t rows, int64_t hidden, float eps, void* stream) {
+    const char* fn = "dit_norm_modulate_fp4";
+    if (!packed || !scales || !x || !scale || !shift || !global_scale_dev)
+        return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);
+    return launch_norm_fp4(fn, nullptr, y, packed, scales, x, nullptr, nullptr, nullptr, scale,
+                           shift, global_scale_dev, rows, hidden, eps, stream);
+}
+
+int dit_scale_residual_norm_modulate_fp4(void* residual_out, void* y, uint8_t* packed,
+                                         uint8_t* scales, const void* x, const void* bias,
+                                         const void* gate, const void* residual,
+                                         const void* scale, const void* shift,
+                                         const float* global_scale_dev, int64_t rows,
+                                         int64_t hidden, float eps, void* stream) {
+    const char* fn = "dit_scale_residual_norm_modulate_fp4";
+    if (!residual_out || !packed || !scales || !x || !gate || !residual || !scale || !shift ||
+        !global_scale_dev)
+        return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);
+    return launch_norm_fp4(fn, residual_out, y, packed, scales, x, bias, gate, residual, scale,
+                           shift, global_scale_dev, rows, hidden, eps, stream);
+}
+
 int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v, const void* img_q,
                      const void* img_k, const void* img_v, int64_t img_rows,
                      int64_t img_row_stride, const void* txt_q, const void* txt_k,

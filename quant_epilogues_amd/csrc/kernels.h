@@ -13,8 +13,9 @@ namespace dit {
 constexpr uint64_t kMaxGridLanes = uint64_t(1) << 32;
 constexpr hipError_t kGridTooLarge = hipErrorInvalidConfiguration;
 
-// LayerNorm + AdaLN modulation + static FP8 (optionally after bias + gated
-// residual). residual == nullptr selects the plain variant.
+// LayerNorm + AdaLN modulation + static FP8 or 16-element-group FP4
+// (optionally after bias + gated residual). residual == nullptr selects the
+// plain variant; fp4 != nullptr selects the FP4 output (q is then nullptr).
 struct NormModulateArgs {
     uint16_t* y;             // [rows, hidden] bf16, or nullptr: not written
     uint8_t* q;              // [rows, hidden] e4m3, or nullptr: not computed
@@ -25,7 +26,11 @@ struct NormModulateArgs {
     const uint16_t* gate;    // [hidden] (residual variant only)
     const uint16_t* scale;   // [hidden]
     const uint16_t* shift;   // [hidden]
-    const float* input_scale;  // device scalar (read only when q is written)
+    const float* input_scale;  // device scalar: FP8 scale (read only when q is written),
+                               // or the FP4 global inverse scale
+    uint8_t* fp4;              // [rows, hidden / 2] packed E2M1, or nullptr (then q / y only)
+    uint8_t* fp4_scales;       // [fp4_rows_padded, hidden / 16] E4M3 group scales
+    int64_t fp4_rows_padded;   // rows rounded up to a multiple of 128
     int64_t rows;
     int32_t hidden;          // multiple of 8, <= kMaxHidden (one thread per 8 columns)
     float eps;

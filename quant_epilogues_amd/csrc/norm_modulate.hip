@@ -62,7 +62,7 @@ __device__ __forceinline__ void col8(const float* cols, const NormModulateArgs& 
     }
 }
 
-template <int MODE, int WPR, int RPW, int V, bool kLds>
+template <int MODE, int WPR, int RPW, int V, bool kLds, bool kFp4>
 __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormModulateArgs a,
                                                                             double inv_hidden) {
     // cols: [kColVecs][hidden] fp32 = 1 + scale, shift, gate, bias
@@ -91,6 +91,7 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
 
     const bool want_y = a.y != nullptr, want_q = a.q != nullptr;  // wave-uniform
     const float inv = want_q ? 1.0f / *a.input_scale : 0.0f;  // IEEE division
+    const float g4 = kFp4 ? *a.input_scale : 0.0f;  // FP4: the global inverse scale
 
     // 2. Column vectors to fp32 in LDS, while the streaming loads are in flight.
     if (kLds) {
@@ -174,7 +175,16 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
             s2 += scratch[rw][w][1];
         }
     }
-    if (!active) return;
+    if (!active) {
+        if constexpr (kFp4) {  // rows [rows, round_up(rows, 128)) of the scale matrix are zero
+            if (row < a.fp4_rows_padded) {
+                const int groups = H >> 4;
+                for (int gi = sw * 64 + lane; gi < groups; gi += 64 * WPR)
+                    a.fp4_scales[row * groups + gi] = 0;
+            }
+        }
+        return;
+    }
     // mean = s1 / hidden within an ulp of binary64 (reciprocal from the host),
     // factor = 1 / sqrt(var + eps) by binary64 Newton steps; both then rounded
     // once to fp32.
@@ -186,11 +196,19 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
     // 5. Modulate, quantise, store.
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        if (!ok[k]) continue;
+        // The FP4 path keeps every lane to the end: the two lanes of a
+        // 16-element group exchange their maxima (columns past the row end
+        // come in whole pairs and only pair with each other).
+        if (!kFp4 && !ok[k]) continue;
         const int c = 64 * (sw + WPR * k) + lane;
         float ops[8], sh[8];
-        col8<kLds>(cols, a, 0, c, ops);
-        col8<kLds>(cols, a, 1, c, sh);
+        if (ok[k]) {
+            col8<kLds>(cols, a, 0, c, ops);
+            col8<kLds>(cols, a, 1, c, sh);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ops[i] = sh[i] = 0.0f;
+        }
         uint32_t yw[4];
         float yv[8];
 #pragma unroll
@@ -203,6 +221,33 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
             yw[i / 2] = pack_bf16(m0, m1);
             yv[i] = bf_lo(yw[i / 2]);
             yv[i + 1] = bf_hi(yw[i / 2]);
+        }
+        if constexpr (kFp4) {
+            // 16-element group = this lane's 8 values and its neighbour's
+            // (lanes 2g and 2g + 1 hold chunks 2g and 2g + 1 of the row).
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(yv[i]));
+            const float other = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false));
+            amax = __builtin_fmaxf(amax, other);  // quad_perm [1, 0, 3, 2]
+            const float s_pre = (amax / 6.0f) * g4;
+            const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                                    __builtin_fminf(s_pre, 448.0f), 0.0f, 0, false) & 0xFFu;
+            uint32_t packed = 0;
+            if (s8 != 0) {
+                const float kq = g4 / e4m3_value_pos(s8);  // IEEE division
+                float t[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = yv[i] * kq;
+                packed = pack_e2m1x8(t);
+            }
+            if (ok[k]) {
+                if (want_y) store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
+                store4(a.fp4 + row * (H >> 1) + 4 * c, packed);
+                if ((lane & 1) == 0) a.fp4_scales[row * (H >> 4) + (c >> 1)] = (uint8_t)s8;
+            }
+            continue;
         }
         if (want_y) store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
         if (want_q) {  // from the bf16 y, stored or not
@@ -217,13 +262,15 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
 
 // Launch with WPR waves per row, RPW rows per workgroup and V chunks per lane
 // (V * 64 * WPR >= hidden / 8); kLds stages the column vectors in LDS.
-template <int MODE, int WPR, int RPW, int V, bool kLds>
+template <int MODE, int WPR, int RPW, int V, bool kLds, bool kFp4>
 hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
-    const uint64_t blocks = (uint64_t)((a.rows + RPW - 1) / RPW);
+    const int64_t grid_rows = kFp4 ? a.fp4_rows_padded : a.rows;
+    const uint64_t blocks = (uint64_t)((grid_rows + RPW - 1) / RPW);
     if (blocks * (64 * WPR * RPW) >= kMaxGridLanes) return kGridTooLarge;
     const size_t lds = kLds ? (size_t)kColVecs<MODE> * a.hidden * sizeof(float) : 0;
-    hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds>), dim3((unsigned)blocks),
-                       dim3(64 * WPR * RPW), lds, stream, a, 1.0 / (double)a.hidden);
+    hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4>),
+                       dim3((unsigned)blocks), dim3(64 * WPR * RPW), lds, stream, a,
+                       1.0 / (double)a.hidden);
     return hipGetLastError();
 }
 
@@ -236,20 +283,20 @@ hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
 //    with both outputs, four waves and one row with the FP8 output only;
 //  - residual variants, many rows: one wave per row, eight rows per workgroup,
 //    column vectors staged in LDS when they fit in 48 KiB.
-template <int MODE>
+template <int MODE, bool kFp4>
 hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
     const int cpr = a.hidden / 8;
     if (a.rows < 1024) {
         switch ((cpr + 383) / 384) {
-            case 1: return launch_geom<MODE, 6, 2, 1, false>(a, stream);
-            case 2: return launch_geom<MODE, 6, 2, 2, false>(a, stream);
-            default: return launch_geom<MODE, 6, 2, 3, false>(a, stream);  // up to 1152 chunks
+            case 1: return launch_geom<MODE, 6, 2, 1, false, kFp4>(a, stream);
+            case 2: return launch_geom<MODE, 6, 2, 2, false, kFp4>(a, stream);
+            default: return launch_geom<MODE, 6, 2, 3, false, kFp4>(a, stream);  // up to 1152 chunks
         }
     }
     if constexpr (MODE == kPlain) {
         if (cpr > 384 && cpr <= 768) {
-            return a.y ? launch_geom<MODE, 6, 2, 2, false>(a, stream)
-                       : launch_geom<MODE, 4, 1, 3, false>(a, stream);
+            return a.y ? launch_geom<MODE, 6, 2, 2, false, kFp4>(a, stream)
+                       : launch_geom<MODE, 4, 1, 3, false, kFp4>(a, stream);
         }
     }
     if constexpr (MODE != kPlain) {
@@ -258,8 +305,8 @@ hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
         switch ((cpr + 63) / 64) {
 #define DIT_NM_ONE_WAVE(VV)                                                                    \
     case VV:                                                                                   \
-        return lds ? launch_geom<MODE, 1, 8, VV, true>(a, stream)                             \
-                   : launch_geom<MODE, 1, 8, VV, false>(a, stream);
+        return lds ? launch_geom<MODE, 1, 8, VV, true, kFp4>(a, stream)                             \
+                   : launch_geom<MODE, 1, 8, VV, false, kFp4>(a, stream);
             DIT_NM_ONE_WAVE(1) DIT_NM_ONE_WAVE(2) DIT_NM_ONE_WAVE(3)
             DIT_NM_ONE_WAVE(4) DIT_NM_ONE_WAVE(5) DIT_NM_ONE_WAVE(6)
 #undef DIT_NM_ONE_WAVE
@@ -267,21 +314,26 @@ hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
     }
 two_waves:
     switch ((cpr + 127) / 128) {
-        case 1: return launch_geom<MODE, 2, 4, 1, false>(a, stream);
-        case 2: return launch_geom<MODE, 2, 4, 2, false>(a, stream);
-        case 3: return launch_geom<MODE, 2, 4, 3, false>(a, stream);
-        case 4: return launch_geom<MODE, 2, 4, 4, false>(a, stream);
-        case 5: case 6: return launch_geom<MODE, 2, 4, 6, false>(a, stream);
-        default: return launch_geom<MODE, 2, 4, 8, false>(a, stream);  // up to 1024 chunks
+        case 1: return launch_geom<MODE, 2, 4, 1, false, kFp4>(a, stream);
+        case 2: return launch_geom<MODE, 2, 4, 2, false, kFp4>(a, stream);
+        case 3: return launch_geom<MODE, 2, 4, 3, false, kFp4>(a, stream);
+        case 4: return launch_geom<MODE, 2, 4, 4, false, kFp4>(a, stream);
+        case 5: case 6: return launch_geom<MODE, 2, 4, 6, false, kFp4>(a, stream);
+        default: return launch_geom<MODE, 2, 4, 8, false, kFp4>(a, stream);  // up to 1024 chunks
     }
+}
+
+template <bool kFp4>
+hipError_t launch_modes(const NormModulateArgs& a, hipStream_t stream) {
+    if (a.residual == nullptr) return launch_mode<kPlain, kFp4>(a, stream);
+    if (a.bias == nullptr) return launch_mode<kResidual, kFp4>(a, stream);
+    return launch_mode<kBiasResidual, kFp4>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_norm_modulate_fp8(const NormModulateArgs& a, hipStream_t stream) {
-    if (a.residual == nullptr) return launch_mode<kPlain>(a, stream);
-    if (a.bias == nullptr) return launch_mode<kResidual>(a, stream);
-    return launch_mode<kBiasResidual>(a, stream);
+    return a.fp4 ? launch_modes<true>(a, stream) : launch_modes<false>(a, stream);
 }
 
 }  // namespace dit

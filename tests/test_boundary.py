@@ -42,7 +42,8 @@ def test_exports_every_declared_symbol(native):
     declared = native.header_symbols()
     assert set(declared) == {
         "dit_abi_version", "dit_status_string", "dit_last_error", "dit_norm_modulate_fp8",
-        "dit_scale_residual_norm_modulate_fp8", "dit_qkv_epilogue", "dit_bias_mul_add",
+        "dit_scale_residual_norm_modulate_fp8", "dit_norm_modulate_fp4",
+        "dit_scale_residual_norm_modulate_fp4", "dit_qkv_epilogue", "dit_bias_mul_add",
         "dit_token_cat_quant",
     }
     raw = ctypes.CDLL(native.LIB_PATH)
@@ -193,3 +194,32 @@ def test_refuses_launches_beyond_the_grid_limit(native):
                None) == native.DIT_ERR_UNSUPPORTED
     assert cat(native.DIT_QUANT_FP4_E2M1, FAKE, FAKE, FAKE, 1 << 28, FAKE2, 16, 4, FAKE,
                None) == native.DIT_ERR_UNSUPPORTED
+
+
+def test_norm_fp4_refusals(native):
+    L = native.lib()
+    f = L.dit_norm_modulate_fp4
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3072, 1e-6, None]
+    bad = list(args)
+    bad[1] = None  # packed
+    assert f(*bad) == native.DIT_ERR_NULL
+    bad = list(args)
+    bad[8] = 3080  # a multiple of 8, not of 16
+    assert f(*bad) == native.DIT_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[1] = FAKE + 8
+    assert f(*bad) == native.DIT_ERR_ALIGN
+    bad = list(args)
+    bad[2] = FAKE + 3  # scales may have any alignment
+    bad[7] = 0
+    assert f(*bad) == native.DIT_OK
+    g = L.dit_scale_residual_norm_modulate_fp4
+    args = [FAKE] * 11 + [4, 3072, 1e-6, None]
+    bad = list(args)
+    bad[6] = None  # gate
+    assert g(*bad) == native.DIT_ERR_NULL
+    bad = list(args)
+    bad[1] = bad[5] = None  # no y, no bias
+    bad[11] = 0
+    assert g(*bad) == native.DIT_OK
+    assert g(*(args[:11] + [1 << 30, 3072, 1e-6, None])) == native.DIT_ERR_UNSUPPORTED

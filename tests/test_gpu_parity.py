@@ -193,6 +193,57 @@ def test_norm_output_selection(qe, oracle_mod, e4m3_table, rows, hidden, input_s
     print("exact: " + " ".join(msg))
 
 
+NORM_FP4_CASES = [
+    # (rows, hidden, residual variant, with_bias, write y, g, seed)
+    (4096, 3072, True, True, True, 448.0, 40),    # Qwen-Image bias + residual norm, NVFP4
+    (4608, 6144, False, False, False, 448.0, 41),  # FLUX.2 width, FP4 only
+    (127, 3072, False, False, True, 1.0, 42),
+    (17, 1008, True, False, True, 448.0, 43),      # 111 pad rows, 126 chunks: a ragged wave
+    (5, 16, False, False, True, 1e4, 44),          # one group per row, saturating scales
+    (1030, 4112, False, False, True, 448.0, 45),   # 514 chunks per row, six-wave geometry
+    (1030, 4112, True, True, False, 448.0, 46),
+]
+
+
+@pytest.mark.parametrize("rows,hidden,resid,with_bias,want_y,g,seed", NORM_FP4_CASES)
+def test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, resid, with_bias, want_y, g, seed):
+    """LayerNorm (optionally after bias + gated residual) with NVFP4 output."""
+    _print_case("norm fp4", rows, hidden, resid, with_bias, want_y, g, seed)
+    gv = float(np.float32(g))
+    rows_pad = (rows + 127) // 128 * 128
+    y = Guarded((rows, hidden), torch.bfloat16) if want_y else None
+    packed = Guarded((rows, hidden // 2), torch.uint8)
+    scales = Guarded((rows_pad, hidden // 16), torch.uint8)
+    if resid:
+        inp = synth.scale_residual_inputs(rows, hidden, seed=seed, with_bias=with_bias)
+        r = Guarded((rows, hidden), torch.bfloat16)
+        qe.dit_scale_residual_norm_modulate_fp4(
+            r.t, y and y.t, packed.t, scales.t, dev(inp.x), dev(inp.bias), dev(inp.gate),
+            dev(inp.residual), dev(inp.scale), dev(inp.shift), dscalar(gv), rows, hidden, inp.eps)
+        rr, ry, rp, rs, s_pre, pre = oracle_mod.scale_residual_norm_modulate_fp4(
+            bits(inp.x), None if inp.bias is None else bits(inp.bias), bits(inp.gate),
+            bits(inp.residual), bits(inp.scale), bits(inp.shift), gv, inp.eps)
+    else:
+        inp = synth.norm_modulate_inputs(rows, hidden, seed=seed)
+        qe.dit_norm_modulate_fp4(y and y.t, packed.t, scales.t, dev(inp.x), dev(inp.scale),
+                                 dev(inp.shift), dscalar(gv), rows, hidden, inp.eps)
+        ry, rp, rs, s_pre, pre = oracle_mod.norm_modulate_fp4(
+            bits(inp.x), bits(inp.scale), bits(inp.shift), gv, inp.eps)
+    torch.cuda.synchronize()
+    msg = []
+    if resid:
+        r.check("r")
+        msg.append(f"r {check_bf16('residual_out', r.bits(), rr):.6f}")
+    if want_y:
+        y.check("y")
+        msg.append(f"y {check_bf16('y', y.bits(), ry):.6f}")
+    packed.check("packed"), scales.check("scales")
+    ec, es = check_fp4("norm fp4", packed.bits(), scales.bits(), rp, rs, s_pre, pre,
+                       oracle_mod.f32_from_bf16(ry), gv, e4m3_table, oracle_mod.e2m1_encode)
+    msg.append(f"codes {ec:.6f} scales {es:.6f}")
+    print("exact: " + " ".join(msg))
+
+
 def test_fp8_split_equals_fused_on_gpu(qe):
     """q of the fused kernel == y re-quantised by the token-cat FP8 path."""
     inp = synth.norm_modulate_inputs(256, 3072, seed=21, input_scale=0.4754464328)
