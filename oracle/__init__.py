@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "oracle_token_cat_fp8": (None, [P, P, P, I64, P, I64, I64, F]),
             "oracle_token_cat_fp4": (None, [P, P, P, P, P, I64, P, I64, I64, F]),
             "oracle_norm_modulate_fp4": (None, [P, P, P, P, P, P, P, P, F, I64, I64, F]),
+            "oracle_fp4_scales_to_128x4": (None, [P, P, I64, I64]),
             "oracle_scale_residual_norm_modulate_fp4":
                 (None, [P, P, P, P, P, P, P, P, P, P, P, P, F, I64, I64, F]),
         }
@@ -311,3 +312,14 @@ def scale_residual_norm_modulate_fp4(x, bias, gate, residual, scale, shift, g: f
         _ptr(r), _ptr(y), _ptr(packed), _ptr(scales), _ptr(s_pre), _ptr(pre), _ptr(x),
         _ptr(bias), _ptr(gate), _ptr(residual), _ptr(scale), _ptr(shift), g, rows, hidden, eps)
     return r, y, packed, scales, s_pre, pre
+
+
+def fp4_scales_to_128x4(scales):
+    """Row-major FP4 scales [rows_padded, groups] -> the 128x4 tile layout, as a
+    flat uint8 array of the same size."""
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows_padded, groups = scales.shape
+    assert rows_padded % 128 == 0 and groups % 4 == 0
+    out = np.empty(scales.size, np.uint8)
+    lib().oracle_fp4_scales_to_128x4(_ptr(out), _ptr(scales), rows_padded, groups)
+    return out

@@ -521,3 +521,30 @@ void oracle_scale_residual_norm_modulate_fp4(
     oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, r_out, scale, shift, g, rows,
                              hidden, eps);
 }
+
+/* ======================================================================== */
+/* FP4 scale layout for FP4 GEMMs                                           */
+/* ======================================================================== */
+
+/* The 128x4 interleaved ("swizzled") scale layout the sglang PR 37141 page
+ * names for its NVFP4 output (get_sf_out_offset_128x4, matching FlashInfer)
+ * without spelling it out. Reading, from the public description of this
+ * block-scale layout for FP4 GEMMs: the [rows_padded, groups] scale matrix
+ * (rows_padded a multiple of 128, groups a multiple of 4) is cut into tiles
+ * of 128 rows x 4 columns, stored one after another, the tile column index
+ * fastest; inside a tile, row m and column k go to byte
+ * (m % 32) * 16 + (m / 32) * 4 + k, i.e. the tile is [32][4][4] over
+ * (m % 32, m / 32, k). Parity unpinned against the third-party layout itself:
+ * the pages print none of its bytes. */
+void oracle_fp4_scales_to_128x4(uint8_t* out, const uint8_t* row_major,
+                                int64_t rows_padded, int64_t groups) {
+    const int64_t tiles_per_row = groups / 4;
+    for (int64_t m = 0; m < rows_padded; ++m) {
+        for (int64_t k = 0; k < groups; ++k) {
+            const int64_t tile = (m / 128) * tiles_per_row + k / 4;
+            const int64_t r = m % 128;
+            const int64_t inner = (r % 32) * 16 + (r / 32) * 4 + k % 4;
+            out[tile * 512 + inner] = row_major[m * groups + k];
+        }
+    }
+}

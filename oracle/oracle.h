@@ -130,6 +130,11 @@ void oracle_scale_residual_norm_modulate_fp4(
     const uint16_t* residual, const uint16_t* scale, const uint16_t* shift,
     float g, int64_t rows, int64_t hidden, float eps);
 
+/* Rearranges a row-major FP4 scale matrix [rows_padded, groups] (rows_padded %
+ * 128 == 0, groups % 4 == 0) into the 128x4 tile layout of FP4 GEMMs. */
+void oracle_fp4_scales_to_128x4(uint8_t* out, const uint8_t* row_major,
+                                int64_t rows_padded, int64_t groups);
+
 #ifdef __cplusplus
 }
 #endif

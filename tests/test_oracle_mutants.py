@@ -90,6 +90,12 @@ MUTANTS = {
         ("memset(scales, 0, (size_t)(rows_padded * groups));", "memset(scales, 0x38, (size_t)(rows_padded * groups));", 2)],
     "norm FP4 quantises the input row instead of y": [
         ("y + r * hidden, hidden, g);", "x + r * hidden, hidden, g);")],
+    "128x4 scale layout with the 32 and 4 row factors swapped": [
+        ("const int64_t inner = (r % 32) * 16 + (r / 32) * 4 + k % 4;",
+         "const int64_t inner = (r % 4) * 128 + (r / 4) * 4 + k % 4;")],
+    "128x4 scale layout with tiles in column order": [
+        ("const int64_t tile = (m / 128) * tiles_per_row + k / 4;",
+         "const int64_t tile = (k / 4) * (rows_padded / 128) + m / 128;")],
     "residual norm FP4 normalises x instead of the new residual": [
         ("oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, r_out, scale, shift, g, rows,",
          "oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, x, scale, shift, g, rows,")],

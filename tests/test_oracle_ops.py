@@ -518,3 +518,37 @@ def test_scale_residual_fp4_is_the_norm_fp4_of_residual_out(oracle_mod):
     assert np.array_equal(r, r8)
     y2, p2, s2, _, _ = oracle_mod.norm_modulate_fp4(r, b(inp.scale), b(inp.shift), 448.0, inp.eps)
     assert np.array_equal(y, y2) and np.array_equal(packed, p2) and np.array_equal(scales, s2)
+
+
+# ---------------------------------------------------------------------------
+# 128x4 FP4 scale layout
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows_padded,groups", [(128, 4), (256, 12), (384, 1536 // 16)])
+def test_fp4_scale_layout_matches_tensor_reshape(oracle_mod, rows_padded, groups):
+    """The layout as a tensor view: [Mt, 128, Kt, 4] -> split the 128 rows as
+    (4, 32) -> order (Mt, Kt, 32, 4, 4). Every byte is a distinct tag, so the
+    comparison checks the whole permutation."""
+    tags = np.arange(rows_padded * groups, dtype=np.int64)
+    s = (tags % 251).astype(np.uint8).reshape(rows_padded, groups)  # byte tags
+    want_idx = (tags.reshape(rows_padded // 128, 4, 32, groups // 4, 4)
+                .transpose(0, 3, 2, 1, 4).reshape(-1))
+    got = oracle_mod.fp4_scales_to_128x4(s)
+    assert np.array_equal(got, s.reshape(-1)[want_idx])
+
+
+def test_fp4_scale_layout_tiles_are_contiguous_and_complete(oracle_mod):
+    """Each 128 x 4 block of the matrix lands in one 512-byte range, blocks
+    in row-major block order, and every byte appears once."""
+    rows_padded, groups = 256, 8
+    ids = np.arange(rows_padded * groups, dtype=np.int64)
+    lo = oracle_mod.fp4_scales_to_128x4((ids & 0xFF).astype(np.uint8).reshape(rows_padded, groups))
+    hi = oracle_mod.fp4_scales_to_128x4((ids >> 8).astype(np.uint8).reshape(rows_padded, groups))
+    back = lo.astype(np.int64) | (hi.astype(np.int64) << 8)
+    assert np.array_equal(np.sort(back), ids)
+    m, k = back // groups, back % groups
+    tile = (m // 128) * (groups // 4) + k // 4
+    assert np.array_equal(tile, np.arange(back.size) // 512)
+    # Inside a tile: the first 16 bytes are rows 0, 32, 64, 96, four scales each.
+    assert list(m[:16]) == [0] * 4 + [32] * 4 + [64] * 4 + [96] * 4
+    assert list(k[:16]) == [0, 1, 2, 3] * 4
