@@ -86,8 +86,9 @@ class Workload:
     # (4096 image + 512 text tokens, 48 heads, one shared [cos | sin] cache),
     # the FP8-only LayerNorm + modulation at the FLUX.2 shape (4608 x 6144, no
     # bf16 output), the bf16-only bias + gated-residual norm (no FP8) and the
-    # same norm with NVFP4 output (4096 x 3072, g = 448).
-    EXTRA = ("qkv_flux2", "norm_flux2_fp8", "sr_norm_bf16", "sr_norm_fp4")
+    # same norm with NVFP4 output (4096 x 3072, g = 448), and the FP4 token
+    # concatenation writing its scales in the 128x4 tile layout.
+    EXTRA = ("qkv_flux2", "norm_flux2_fp8", "sr_norm_bf16", "sr_norm_fp4", "cat_fp4_128x4")
 
     def __init__(self, torch, qe, seed=0, names=ALL):
         import numpy as np
@@ -169,7 +170,7 @@ class Workload:
             scales = empty((IMG + 127) // 128 * 128, H // 16, dtype=torch.uint8)
             p = P(r, y, packed, scales, x, b, gt, res, sc, sh, scalar(448.0))
             return bytes_sr_fp4(IMG, H), lambda: qe.dit_scale_residual_norm_modulate_fp4(
-                *p, IMG, H, 1e-6, stream=st)
+                *p[:4], qe.DIT_FP4_SCALES_ROW_MAJOR, *p[4:], IMG, H, 1e-6, stream=st)
 
         def bma():
             R = IMG + TXT
@@ -203,6 +204,7 @@ class Workload:
             "norm_flux2_fp8": lambda: norm(FLUX_ROWS, FLUX_A, want_y=False),
             "sr_norm_bf16": lambda: sr_norm(want_q=False),
             "sr_norm_fp4": sr_norm_fp4,
+            "cat_fp4_128x4": lambda: cat(qe.DIT_QUANT_FP4_E2M1_128X4),
         }
         self.launches = []  # (name, compulsory bytes, launch)
         for n in names:
@@ -276,7 +278,7 @@ KERNEL_SOURCES = {
     "qkv": "qkv_epilogue.hip", "bma": "bias_mul_add.hip", "cat_fp8": "token_cat_quant.hip",
     "cat_fp4": "token_cat_quant.hip", "qkv_flux2": "qkv_epilogue.hip",
     "norm_flux2_fp8": "norm_modulate.hip", "sr_norm_bf16": "norm_modulate.hip",
-    "sr_norm_fp4": "norm_modulate.hip",
+    "sr_norm_fp4": "norm_modulate.hip", "cat_fp4_128x4": "token_cat_quant.hip",
 }
 
 

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 3
+#define DIT_ABI_VERSION 4
 
 typedef enum dit_status {
     DIT_OK = 0,
@@ -121,6 +121,22 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
                                          void* stream);
 
 /*
+ * Layouts of the FP4 group-scale matrix of rows_padded = round_up(rows, 128)
+ * rows and groups = columns / 16 scales per row:
+ *   DIT_FP4_SCALES_ROW_MAJOR  scale (m, k) at byte m * groups + k
+ *   DIT_FP4_SCALES_128X4      the tile layout FP4 GEMMs read, which the sglang
+ *       PR 37141 page names (128x4, as FlashInfer) without spelling out; read
+ *       as: 128-row x 4-column tiles of 512 bytes, tile (m / 128, k / 4) at
+ *       byte ((m / 128) * (groups / 4) + k / 4) * 512, and inside it scale
+ *       (m, k) at (m % 32) * 16 + ((m / 32) % 4) * 4 + k % 4. Needs groups % 4
+ *       == 0 (columns a multiple of 64).
+ * Either way the buffer holds rows_padded * groups bytes and the scales of
+ * rows [rows, rows_padded) are 0x00.
+ */
+#define DIT_FP4_SCALES_ROW_MAJOR 0
+#define DIT_FP4_SCALES_128X4 1
+
+/*
  * LayerNorm + AdaLN modulation with NVFP4 output: the bf16 y of
  * dit_norm_modulate_fp8, quantised in 16-element groups exactly as the FP4
  * output of dit_token_cat_quant (E2M1 codes, one E4M3 scale per group from
@@ -134,8 +150,10 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
  *
  *   y       [rows, hidden] bf16, out; NULLABLE (then only the FP4 output)
  *   packed  [rows, hidden / 2] bytes, out; element 2k in the low nibble
- *   scales  [round_up(rows, 128), hidden / 16] E4M3 bytes, out, row-major;
- *           rows [rows, round_up(rows, 128)) are written as 0x00
+ *   scales  [round_up(rows, 128), hidden / 16] E4M3 bytes, out, in the layout
+ *           scale_layout names; scales of pad rows are written as 0x00
+ *   scale_layout  DIT_FP4_SCALES_ROW_MAJOR or DIT_FP4_SCALES_128X4 (then
+ *           hidden must be a multiple of 64)
  *   x, scale, shift, eps  as dit_norm_modulate_fp8
  *   global_scale_dev  device fp32 scalar g: group scale e4m3(amax / 6 * g),
  *           element code e2m1(y * g / scale)
@@ -143,9 +161,10 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
  * hidden must be a multiple of 16 and at most 8192 (else DIT_ERR_UNSUPPORTED).
  * scales needs no alignment; the other tensors 16 bytes.
  */
-int dit_norm_modulate_fp4(void* y, uint8_t* packed, uint8_t* scales, const void* x,
-                          const void* scale, const void* shift, const float* global_scale_dev,
-                          int64_t rows, int64_t hidden, float eps, void* stream);
+int dit_norm_modulate_fp4(void* y, uint8_t* packed, uint8_t* scales, int32_t scale_layout,
+                          const void* x, const void* scale, const void* shift,
+                          const float* global_scale_dev, int64_t rows, int64_t hidden,
+                          float eps, void* stream);
 
 /*
  * Optional input bias + gated residual, then the same LayerNorm + modulation
@@ -156,7 +175,8 @@ int dit_norm_modulate_fp4(void* y, uint8_t* packed, uint8_t* scales, const void*
  * of the sglang PR 37156 and PR 37116 pages.
  */
 int dit_scale_residual_norm_modulate_fp4(void* residual_out, void* y, uint8_t* packed,
-                                         uint8_t* scales, const void* x, const void* bias,
+                                         uint8_t* scales, int32_t scale_layout,
+                                         const void* x, const void* bias,
                                          const void* gate, const void* residual,
                                          const void* scale, const void* shift,
                                          const float* global_scale_dev, int64_t rows,
@@ -229,7 +249,8 @@ int dit_bias_mul_add(void* y, const void* x, const void* bias, const void* gate,
 
 /* Quantisation kinds of dit_token_cat_quant. */
 #define DIT_QUANT_FP8_E4M3 0
-#define DIT_QUANT_FP4_E2M1 1
+#define DIT_QUANT_FP4_E2M1 1        /* FP4, group scales row-major            */
+#define DIT_QUANT_FP4_E2M1_128X4 2  /* FP4, group scales in 128x4 tiles       */
 
 /*
  * Token concatenation [a | b] fused with static FP8 or 16-element-group FP4
@@ -243,7 +264,9 @@ int dit_bias_mul_add(void* y, const void* x, const void* bias, const void* gate,
  * group, zero scales for pad rows; the global scale argument is an inverse
  * scale).
  *
- *   kind      DIT_QUANT_FP8_E4M3 or DIT_QUANT_FP4_E2M1
+ *   kind      DIT_QUANT_FP8_E4M3, DIT_QUANT_FP4_E2M1 (row-major scales) or
+ *             DIT_QUANT_FP4_E2M1_128X4 (scales in the 128x4 tile layout, see
+ *             DIT_FP4_SCALES_128X4; a_cols + b_cols must be a multiple of 64)
  *   out       FP8: [rows, a_cols + b_cols] E4M3 bytes
  *             FP4: [rows, (a_cols + b_cols) / 2] bytes, element 2k in the low
  *             nibble of byte k, element 2k+1 in the high nibble

@@ -19,7 +19,8 @@ import torch
 
 from ._native import (  # noqa: F401
     DIT_ERR_ALIGN, DIT_ERR_HIP, DIT_ERR_NULL, DIT_ERR_SHAPE, DIT_ERR_UNSUPPORTED, DIT_OK,
-    DIT_QUANT_FP4_E2M1, DIT_QUANT_FP8_E4M3, LIB_PATH, DitError, dit_bias_mul_add,
+    DIT_FP4_SCALES_128X4, DIT_FP4_SCALES_ROW_MAJOR, DIT_QUANT_FP4_E2M1,
+    DIT_QUANT_FP4_E2M1_128X4, DIT_QUANT_FP8_E4M3, LIB_PATH, DitError, dit_bias_mul_add,
     dit_norm_modulate_fp4, dit_norm_modulate_fp8, dit_qkv_epilogue,
     dit_scale_residual_norm_modulate_fp4, dit_scale_residual_norm_modulate_fp8,
     dit_token_cat_quant, header_symbols, last_error, lib, status_string,
@@ -88,7 +89,8 @@ def _fp4_outputs(x):
 
 
 def norm_modulate_fp4(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
-                      global_scale: torch.Tensor, eps: float = 1e-6, want_y: bool = True):
+                      global_scale: torch.Tensor, eps: float = 1e-6, want_y: bool = True,
+                      scale_layout: int = DIT_FP4_SCALES_ROW_MAJOR):
     """LayerNorm (no affine) + AdaLN scale/shift + 16-element-group FP4: returns
     (y or None, packed [rows, hidden/2], scales [round_up(rows,128), hidden/16])."""
     for t, n in ((x, "x"), (scale, "scale"), (shift, "shift")):
@@ -97,13 +99,14 @@ def norm_modulate_fp4(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
     hidden = x.shape[-1]
     y = torch.empty_like(x) if want_y else None
     packed, scales = _fp4_outputs(x)
-    dit_norm_modulate_fp4(y, packed, scales, x, scale, shift, global_scale, x.numel() // hidden,
-                          hidden, eps)
+    dit_norm_modulate_fp4(y, packed, scales, scale_layout, x, scale, shift, global_scale,
+                          x.numel() // hidden, hidden, eps)
     return y, packed, scales
 
 
 def scale_residual_norm_modulate_fp4(x, bias, gate, residual, scale, shift, global_scale,
-                                     eps: float = 1e-6, want_y: bool = True):
+                                     eps: float = 1e-6, want_y: bool = True,
+                                     scale_layout: int = DIT_FP4_SCALES_ROW_MAJOR):
     """bias (optional) + gated residual, then norm/modulate/FP4: returns
     (residual_out, y or None, packed, scales)."""
     for t, n in ((x, "x"), (gate, "gate"), (residual, "residual"), (scale, "scale"),
@@ -116,8 +119,9 @@ def scale_residual_norm_modulate_fp4(x, bias, gate, residual, scale, shift, glob
     r = torch.empty_like(x)
     y = torch.empty_like(x) if want_y else None
     packed, scales = _fp4_outputs(x)
-    dit_scale_residual_norm_modulate_fp4(r, y, packed, scales, x, bias, gate, residual, scale,
-                                         shift, global_scale, x.numel() // hidden, hidden, eps)
+    dit_scale_residual_norm_modulate_fp4(r, y, packed, scales, scale_layout, x, bias, gate,
+                                         residual, scale, shift, global_scale,
+                                         x.numel() // hidden, hidden, eps)
     return r, y, packed, scales
 
 
@@ -178,7 +182,9 @@ def token_cat_quant(kind: int, a: torch.Tensor, b: torch.Tensor | None,
                     scale: torch.Tensor):
     """Quantise the row concatenation [a | b]. FP8: returns the E4M3 bytes
     [rows, cols]. FP4: returns (packed [rows, cols/2], scales
-    [round_up(rows, 128), cols/16]); `scale` is then the global inverse scale."""
+    [round_up(rows, 128), cols/16]); `scale` is then the global inverse scale.
+    With DIT_QUANT_FP4_E2M1_128X4 the scales buffer holds the same bytes in the
+    128x4 tile layout."""
     _dense_bf16(a, "a")
     if b is not None:
         _dense_bf16(b, "b")

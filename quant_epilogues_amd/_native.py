@@ -25,6 +25,9 @@ DIT_ERR_UNSUPPORTED = 4
 DIT_ERR_HIP = 5
 DIT_QUANT_FP8_E4M3 = 0
 DIT_QUANT_FP4_E2M1 = 1
+DIT_QUANT_FP4_E2M1_128X4 = 2
+DIT_FP4_SCALES_ROW_MAJOR = 0
+DIT_FP4_SCALES_128X4 = 1
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -41,9 +44,10 @@ _SIGNATURES = {
     "dit_qkv_epilogue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _I64,
                                         _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32,
                                         _F, _F, _P]),
-    "dit_norm_modulate_fp4": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
+    "dit_norm_modulate_fp4":
+        (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P, _P, _I64, _I64, _F, _P]),
     "dit_scale_residual_norm_modulate_fp4":
-        (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
+        (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
     "dit_bias_mul_add": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _P]),
     "dit_token_cat_quant": (ctypes.c_int, [_I32, _P, _P, _P, _I64, _P, _I64, _I64, _P, _P]),
 }
@@ -142,20 +146,20 @@ def dit_qkv_epilogue(joint_q, joint_k, joint_v, img_q, img_k, img_v, img_rows, i
         head_dim, img_eps, txt_eps, _stream(stream, joint_q)))
 
 
-def dit_norm_modulate_fp4(y, packed, scales, x, scale, shift, global_scale_dev, rows, hidden,
-                          eps, stream=None) -> None:
+def dit_norm_modulate_fp4(y, packed, scales, scale_layout, x, scale, shift, global_scale_dev,
+                          rows, hidden, eps, stream=None) -> None:
     _check(lib().dit_norm_modulate_fp4(
-        _ptr(y), _ptr(packed), _ptr(scales), _ptr(x), _ptr(scale), _ptr(shift),
+        _ptr(y), _ptr(packed), _ptr(scales), scale_layout, _ptr(x), _ptr(scale), _ptr(shift),
         _ptr(global_scale_dev), rows, hidden, eps, _stream(stream, x)))
 
 
-def dit_scale_residual_norm_modulate_fp4(residual_out, y, packed, scales, x, bias, gate,
-                                         residual, scale, shift, global_scale_dev, rows, hidden,
-                                         eps, stream=None) -> None:
+def dit_scale_residual_norm_modulate_fp4(residual_out, y, packed, scales, scale_layout, x, bias,
+                                         gate, residual, scale, shift, global_scale_dev, rows,
+                                         hidden, eps, stream=None) -> None:
     _check(lib().dit_scale_residual_norm_modulate_fp4(
-        _ptr(residual_out), _ptr(y), _ptr(packed), _ptr(scales), _ptr(x), _ptr(bias), _ptr(gate),
-        _ptr(residual), _ptr(scale), _ptr(shift), _ptr(global_scale_dev), rows, hidden, eps,
-        _stream(stream, x)))
+        _ptr(residual_out), _ptr(y), _ptr(packed), _ptr(scales), scale_layout, _ptr(x),
+        _ptr(bias), _ptr(gate), _ptr(residual), _ptr(scale), _ptr(shift), _ptr(global_scale_dev),
+        rows, hidden, eps, _stream(stream, x)))
 
 
 def dit_bias_mul_add(y, x, bias, gate, residual, rows, hidden, stream=None) -> None:

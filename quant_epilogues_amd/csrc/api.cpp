@@ -141,7 +141,8 @@ int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q
 }
 
 static int launch_norm_fp4(const char* fn, void* residual_out, void* y, uint8_t* packed,
-                           uint8_t* scales, const void* x, const void* bias, const void* gate,
+                           uint8_t* scales, int32_t scale_layout, const void* x,
+                           const void* bias, const void* gate,
                            const void* residual, const void* scale, const void* shift,
                            const float* g_dev, int64_t rows, int64_t hidden, float eps,
                            void* stream) {
@@ -149,6 +150,10 @@ static int launch_norm_fp4(const char* fn, void* residual_out, void* y, uint8_t*
     if (hidden % 16 != 0)
         return fail(DIT_ERR_UNSUPPORTED, "%s: hidden (%lld) must be a multiple of 16 (FP4 groups)",
                     fn, (long long)hidden);
+    if (scale_layout != DIT_FP4_SCALES_ROW_MAJOR && scale_layout != DIT_FP4_SCALES_128X4)
+        return fail(DIT_ERR_UNSUPPORTED, "%s: unknown scale layout %d", fn, scale_layout);
+    if (scale_layout == DIT_FP4_SCALES_128X4 && hidden % 64 != 0)
+        return fail(DIT_ERR_UNSUPPORTED, "%s: the 128x4 scale layout needs hidden %% 64 == 0", fn);
     if (!aligned(y, 16) || !aligned(packed, 16) || !aligned(x, 16) || (bias && !aligned(bias, 16)) ||
         !aligned(gate, 16) || !aligned(residual, 16) || !aligned(residual_out, 16) ||
         !aligned(scale, 16) || !aligned(shift, 16) || !aligned(g_dev, 4))
@@ -168,6 +173,7 @@ static int launch_norm_fp4(const char* fn, void* residual_out, void* y, uint8_t*
     a.fp4 = packed;
     a.fp4_scales = scales;
     a.fp4_rows_padded = (rows + 127) / 128 * 128;
+    a.fp4_tiled = scale_layout == DIT_FP4_SCALES_128X4;
     a.rows = rows;
     a.hidden = (int32_t)hidden;
     a.eps = eps;
@@ -175,18 +181,20 @@ static int launch_norm_fp4(const char* fn, void* residual_out, void* y, uint8_t*
     return launched(dit::launch_norm_modulate_fp8(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-int dit_norm_modulate_fp4(void* y, uint8_t* packed, uint8_t* scales, const void* x,
-                          const void* scale, const void* shift, const float* global_scale_dev,
-                          int64_t rows, int64_t hidden, float eps, void* stream) {
+int dit_norm_modulate_fp4(void* y, uint8_t* packed, uint8_t* scales, int32_t scale_layout,
+                          const void* x, const void* scale, const void* shift,
+                          const float* global_scale_dev, int64_t rows, int64_t hidden,
+                          float eps, void* stream) {
     const char* fn = "dit_norm_modulate_fp4";
     if (!packed || !scales || !x || !scale || !shift || !global_scale_dev)
         return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);
-    return launch_norm_fp4(fn, nullptr, y, packed, scales, x, nullptr, nullptr, nullptr, scale,
-                           shift, global_scale_dev, rows, hidden, eps, stream);
+    return launch_norm_fp4(fn, nullptr, y, packed, scales, scale_layout, x, nullptr, nullptr,
+                           nullptr, scale, shift, global_scale_dev, rows, hidden, eps, stream);
 }
 
 int dit_scale_residual_norm_modulate_fp4(void* residual_out, void* y, uint8_t* packed,
-                                         uint8_t* scales, const void* x, const void* bias,
+                                         uint8_t* scales, int32_t scale_layout,
+                                         const void* x, const void* bias,
                                          const void* gate, const void* residual,
                                          const void* scale, const void* shift,
                                          const float* global_scale_dev, int64_t rows,
@@ -195,8 +203,8 @@ int dit_scale_residual_norm_modulate_fp4(void* residual_out, void* y, uint8_t* p
     if (!residual_out || !packed || !scales || !x || !gate || !residual || !scale || !shift ||
         !global_scale_dev)
         return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);
-    return launch_norm_fp4(fn, residual_out, y, packed, scales, x, bias, gate, residual, scale,
-                           shift, global_scale_dev, rows, hidden, eps, stream);
+    return launch_norm_fp4(fn, residual_out, y, packed, scales, scale_layout, x, bias, gate,
+                           residual, scale, shift, global_scale_dev, rows, hidden, eps, stream);
 }
 
 int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v, const void* img_q,
@@ -307,8 +315,9 @@ int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales, const v
                         int64_t a_cols, const void* b, int64_t b_cols, int64_t rows,
                         const float* scale_dev, void* stream) {
     const char* fn = "dit_token_cat_quant";
-    if (kind != DIT_QUANT_FP8_E4M3 && kind != DIT_QUANT_FP4_E2M1)
+    if (kind != DIT_QUANT_FP8_E4M3 && kind != DIT_QUANT_FP4_E2M1 && kind != DIT_QUANT_FP4_E2M1_128X4)
         return fail(DIT_ERR_UNSUPPORTED, "%s: unknown quantisation kind %d", fn, kind);
+    const bool fp4 = kind != DIT_QUANT_FP8_E4M3;
     if (rows < 0 || a_cols < 0 || b_cols < 0)
         return fail(DIT_ERR_SHAPE, "%s: sizes must be >= 0", fn);
     if (a_cols % 16 != 0 || b_cols % 16 != 0 || a_cols < 16)
@@ -316,8 +325,11 @@ int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales, const v
                     fn, (long long)a_cols, (long long)b_cols);
     if (a_cols + b_cols > (int64_t(1) << 28) || rows > kMaxRows)
         return fail(DIT_ERR_UNSUPPORTED, "%s: shape too large", fn);
+    if (kind == DIT_QUANT_FP4_E2M1_128X4 && (a_cols + b_cols) % 64 != 0)
+        return fail(DIT_ERR_UNSUPPORTED, "%s: the 128x4 scale layout needs a_cols + b_cols %% 64 == 0",
+                    fn);
     if (!out || !a || !scale_dev || (b_cols > 0 && !b) ||
-        (kind == DIT_QUANT_FP4_E2M1 && !out_scales))
+        (fp4 && !out_scales))
         return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);
     if (!aligned(out, 16) || !aligned(a, 16) || (b_cols > 0 && !aligned(b, 16)) ||
         !aligned(scale_dev, 4))
@@ -334,6 +346,7 @@ int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales, const v
     t.scale = scale_dev;
     clear_stale_hip_error();
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    t.scales_tiled = kind == DIT_QUANT_FP4_E2M1_128X4;
     return launched(kind == DIT_QUANT_FP8_E4M3 ? dit::launch_token_cat_fp8(t, s)
                                                : dit::launch_token_cat_fp4(t, s),
                     fn);

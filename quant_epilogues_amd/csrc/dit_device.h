@@ -165,6 +165,14 @@ __device__ __forceinline__ uint32_t pack_e2m1x8(const float (&t)[8]) {
     return w;
 }
 
+// Byte offset of scale (m, k) of an FP4 group-scale matrix with `groups`
+// scales per row: row-major, or 128-row x 4-column tiles of 512 bytes (tile
+// column fastest) with rows interleaved as (m % 32, (m / 32) % 4) inside.
+__device__ __forceinline__ int64_t fp4_scale_offset(int64_t m, int k, int groups, bool tiled) {
+    if (!tiled) return m * groups + k;
+    return ((m >> 7) * (groups >> 2) + (k >> 2)) * 512 + (m & 31) * 16 + ((m >> 5) & 3) * 4 + (k & 3);
+}
+
 // ---- reciprocal square root -------------------------------------------------
 
 // RN32(1 / sqrt(v)) for v > 0 within the fp32 range: fp32 reciprocal-sqrt seed,

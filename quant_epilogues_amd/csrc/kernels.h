@@ -31,6 +31,7 @@ struct NormModulateArgs {
     uint8_t* fp4;              // [rows, hidden / 2] packed E2M1, or nullptr (then q / y only)
     uint8_t* fp4_scales;       // [fp4_rows_padded, hidden / 16] E4M3 group scales
     int64_t fp4_rows_padded;   // rows rounded up to a multiple of 128
+    bool fp4_tiled;            // scales in 128x4 tiles (else row-major)
     int64_t rows;
     int32_t hidden;          // multiple of 8, <= kMaxHidden (one thread per 8 columns)
     float eps;
@@ -73,6 +74,7 @@ hipError_t launch_bias_mul_add(const BiasMulAddArgs& a, hipStream_t stream);
 struct TokenCatArgs {
     uint8_t* out;
     uint8_t* out_scales;   // FP4 only
+    bool scales_tiled;     // FP4: scales in 128x4 tiles (else row-major)
     const uint16_t* a;
     const uint16_t* b;
     int64_t a_cols, b_cols, rows;

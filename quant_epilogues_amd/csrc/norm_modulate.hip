@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
             if (row < a.fp4_rows_padded) {
                 const int groups = H >> 4;
                 for (int gi = sw * 64 + lane; gi < groups; gi += 64 * WPR)
-                    a.fp4_scales[row * groups + gi] = 0;
+                    a.fp4_scales[fp4_scale_offset(row, gi, groups, a.fp4_tiled)] = 0;
             }
         }
         return;
@@ -245,7 +245,8 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
             if (ok[k]) {
                 if (want_y) store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
                 store4(a.fp4 + row * (H >> 1) + 4 * c, packed);
-                if ((lane & 1) == 0) a.fp4_scales[row * (H >> 4) + (c >> 1)] = (uint8_t)s8;
+                if ((lane & 1) == 0)
+                    a.fp4_scales[fp4_scale_offset(row, c >> 1, H >> 4, a.fp4_tiled)] = (uint8_t)s8;
             }
             continue;
         }

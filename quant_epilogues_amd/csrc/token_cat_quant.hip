@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a, in
     const int groups = (int)(cols >> 4);
     const int g = tile * kTile + threadIdx.x;
     if (g >= groups) return;
-    uint8_t* scale_out = a.out_scales + row * groups + g;
+    uint8_t* scale_out = a.out_scales + fp4_scale_offset(row, g, groups, a.scales_tiled);
     if (row >= a.rows) {  // pad rows of the scale matrix
         *scale_out = 0;
         return;

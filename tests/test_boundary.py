@@ -199,27 +199,43 @@ def test_refuses_launches_beyond_the_grid_limit(native):
 def test_norm_fp4_refusals(native):
     L = native.lib()
     f = L.dit_norm_modulate_fp4
-    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3072, 1e-6, None]
+    row_major, tiled = native.DIT_FP4_SCALES_ROW_MAJOR, native.DIT_FP4_SCALES_128X4
+    args = [FAKE, FAKE, FAKE, row_major, FAKE, FAKE, FAKE, FAKE, 4, 3072, 1e-6, None]
     bad = list(args)
     bad[1] = None  # packed
     assert f(*bad) == native.DIT_ERR_NULL
     bad = list(args)
-    bad[8] = 3080  # a multiple of 8, not of 16
+    bad[9] = 3080  # a multiple of 8, not of 16
+    assert f(*bad) == native.DIT_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[3], bad[9] = tiled, 3088  # 193 groups: not whole 128x4 tiles
+    assert f(*bad) == native.DIT_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[3] = 7  # no such layout
     assert f(*bad) == native.DIT_ERR_UNSUPPORTED
     bad = list(args)
     bad[1] = FAKE + 8
     assert f(*bad) == native.DIT_ERR_ALIGN
     bad = list(args)
     bad[2] = FAKE + 3  # scales may have any alignment
-    bad[7] = 0
+    bad[8] = 0
     assert f(*bad) == native.DIT_OK
     g = L.dit_scale_residual_norm_modulate_fp4
-    args = [FAKE] * 11 + [4, 3072, 1e-6, None]
+    args = [FAKE] * 4 + [row_major] + [FAKE] * 7 + [4, 3072, 1e-6, None]
     bad = list(args)
-    bad[6] = None  # gate
+    bad[7] = None  # gate
     assert g(*bad) == native.DIT_ERR_NULL
     bad = list(args)
-    bad[1] = bad[5] = None  # no y, no bias
-    bad[11] = 0
+    bad[1] = bad[6] = None  # no y, no bias
+    bad[12] = 0
     assert g(*bad) == native.DIT_OK
-    assert g(*(args[:11] + [1 << 30, 3072, 1e-6, None])) == native.DIT_ERR_UNSUPPORTED
+    assert g(*(args[:12] + [1 << 30, 3072, 1e-6, None])) == native.DIT_ERR_UNSUPPORTED
+
+
+def test_token_cat_tiled_scales_need_whole_tiles(native):
+    L = native.lib()
+    f = L.dit_token_cat_quant
+    tiled = native.DIT_QUANT_FP4_E2M1_128X4
+    assert f(tiled, FAKE, FAKE, FAKE, 6144, FAKE2, 16, 4, FAKE, None) == native.DIT_ERR_UNSUPPORTED
+    assert f(tiled, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, 0, FAKE, None) == native.DIT_OK
+    assert f(3, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_UNSUPPORTED

@@ -194,21 +194,26 @@ def test_norm_output_selection(qe, oracle_mod, e4m3_table, rows, hidden, input_s
 
 
 NORM_FP4_CASES = [
-    # (rows, hidden, residual variant, with_bias, write y, g, seed)
-    (4096, 3072, True, True, True, 448.0, 40),    # Qwen-Image bias + residual norm, NVFP4
-    (4608, 6144, False, False, False, 448.0, 41),  # FLUX.2 width, FP4 only
-    (127, 3072, False, False, True, 1.0, 42),
-    (17, 1008, True, False, True, 448.0, 43),      # 111 pad rows, 126 chunks: a ragged wave
-    (5, 16, False, False, True, 1e4, 44),          # one group per row, saturating scales
-    (1030, 4112, False, False, True, 448.0, 45),   # 514 chunks per row, six-wave geometry
-    (1030, 4112, True, True, False, 448.0, 46),
+    # (rows, hidden, residual variant, with_bias, write y, g, 128x4 scales, seed)
+    (4096, 3072, True, True, True, 448.0, False, 40),    # Qwen-Image bias + residual norm
+    (4096, 3072, True, True, False, 448.0, True, 47),    # the same, 128x4 scales, FP4 only
+    (4608, 6144, False, False, False, 448.0, False, 41),  # FLUX.2 width, FP4 only
+    (127, 3072, False, False, True, 1.0, True, 42),       # one partial 128-row tile
+    (17, 1008, True, False, True, 448.0, False, 43),     # 111 pad rows, 126 chunks: a ragged wave
+    (5, 16, False, False, True, 1e4, False, 44),         # one group per row, saturating scales
+    (1030, 4112, False, False, True, 448.0, False, 45),  # 514 chunks per row, six-wave geometry
+    (1030, 4112, True, True, False, 448.0, False, 46),
+    (300, 4096, False, False, True, 448.0, True, 48),    # three row tiles, 64 tile columns
 ]
 
 
-@pytest.mark.parametrize("rows,hidden,resid,with_bias,want_y,g,seed", NORM_FP4_CASES)
-def test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, resid, with_bias, want_y, g, seed):
-    """LayerNorm (optionally after bias + gated residual) with NVFP4 output."""
-    _print_case("norm fp4", rows, hidden, resid, with_bias, want_y, g, seed)
+@pytest.mark.parametrize("rows,hidden,resid,with_bias,want_y,g,tiled,seed", NORM_FP4_CASES)
+def test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, resid, with_bias, want_y, g, tiled,
+                  seed):
+    """LayerNorm (optionally after bias + gated residual) with NVFP4 output; the
+    128x4 scale layout is checked as the oracle's row-major scales rearranged."""
+    _print_case("norm fp4", rows, hidden, resid, with_bias, want_y, g, tiled, seed)
+    layout = qe.DIT_FP4_SCALES_128X4 if tiled else qe.DIT_FP4_SCALES_ROW_MAJOR
     gv = float(np.float32(g))
     rows_pad = (rows + 127) // 128 * 128
     y = Guarded((rows, hidden), torch.bfloat16) if want_y else None
@@ -218,15 +223,15 @@ def test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, resid, with_bias, wa
         inp = synth.scale_residual_inputs(rows, hidden, seed=seed, with_bias=with_bias)
         r = Guarded((rows, hidden), torch.bfloat16)
         qe.dit_scale_residual_norm_modulate_fp4(
-            r.t, y and y.t, packed.t, scales.t, dev(inp.x), dev(inp.bias), dev(inp.gate),
+            r.t, y and y.t, packed.t, scales.t, layout, dev(inp.x), dev(inp.bias), dev(inp.gate),
             dev(inp.residual), dev(inp.scale), dev(inp.shift), dscalar(gv), rows, hidden, inp.eps)
         rr, ry, rp, rs, s_pre, pre = oracle_mod.scale_residual_norm_modulate_fp4(
             bits(inp.x), None if inp.bias is None else bits(inp.bias), bits(inp.gate),
             bits(inp.residual), bits(inp.scale), bits(inp.shift), gv, inp.eps)
     else:
         inp = synth.norm_modulate_inputs(rows, hidden, seed=seed)
-        qe.dit_norm_modulate_fp4(y and y.t, packed.t, scales.t, dev(inp.x), dev(inp.scale),
-                                 dev(inp.shift), dscalar(gv), rows, hidden, inp.eps)
+        qe.dit_norm_modulate_fp4(y and y.t, packed.t, scales.t, layout, dev(inp.x),
+                                 dev(inp.scale), dev(inp.shift), dscalar(gv), rows, hidden, inp.eps)
         ry, rp, rs, s_pre, pre = oracle_mod.norm_modulate_fp4(
             bits(inp.x), bits(inp.scale), bits(inp.shift), gv, inp.eps)
     torch.cuda.synchronize()
@@ -238,7 +243,11 @@ def test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, resid, with_bias, wa
         y.check("y")
         msg.append(f"y {check_bf16('y', y.bits(), ry):.6f}")
     packed.check("packed"), scales.check("scales")
-    ec, es = check_fp4("norm fp4", packed.bits(), scales.bits(), rp, rs, s_pre, pre,
+    gs = scales.bits()
+    if tiled:  # the same scale bytes, rearranged: compare in the tile layout
+        check_exact("128x4 scales", gs.reshape(-1), oracle_mod.fp4_scales_to_128x4(rs))
+        gs = rs  # the codes are then checked against the row-major scales
+    ec, es = check_fp4("norm fp4", packed.bits(), gs, rp, rs, s_pre, pre,
                        oracle_mod.f32_from_bf16(ry), gv, e4m3_table, oracle_mod.e2m1_encode)
     msg.append(f"codes {ec:.6f} scales {es:.6f}")
     print("exact: " + " ".join(msg))
@@ -487,6 +496,36 @@ def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed
     rs_full = np.concatenate([rs[:len(sel)], np.zeros((rows_pad - rows, cols // 16), np.uint8)])
     ec, es = check_fp4("fp4", gp[sel], gs_sel, rp, rs_full, s_pre, pre, x, gv, e4m3_table,
                        oracle_mod.e2m1_encode)
+    print(f"exact: codes {ec:.6f} scales {es:.6f}")
+
+
+@pytest.mark.parametrize("rows,a_cols,b_cols,seed", [(4608, 6144, 18432, 50), (130, 64, 192, 51)])
+def test_token_cat_fp4_128x4_scales(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, seed):
+    """FP4 token concatenation with the scales in the 128x4 tile layout: the
+    packed codes equal the row-major run's and the scale bytes equal the
+    oracle's row-major scales rearranged into tiles (pad rows included)."""
+    _print_case("token_cat_fp4 128x4", rows, a_cols, b_cols, seed)
+    inp = synth.token_cat_inputs(rows, a_cols, b_cols, seed=seed)
+    cols, rows_pad = a_cols + b_cols, (rows + 127) // 128 * 128
+    packed = Guarded((rows, cols // 2), torch.uint8)
+    scales = Guarded((rows_pad, cols // 16), torch.uint8)
+    qe.dit_token_cat_quant(qe.DIT_QUANT_FP4_E2M1_128X4, packed.t, scales.t, dev(inp.attn), a_cols,
+                           dev(inp.mlp), b_cols, rows, dscalar(inp.fp4_g))
+    ref_packed, ref_scales = qe.token_cat_quant(qe.DIT_QUANT_FP4_E2M1, dev(inp.attn),
+                                                dev(inp.mlp), dscalar(inp.fp4_g))
+    torch.cuda.synchronize()
+    packed.check("packed"), scales.check("scales")
+    check_exact("packed", packed.bits(), ref_packed.cpu().numpy())
+    gs = ref_scales.cpu().numpy()
+    check_exact("128x4 scales", scales.bits().reshape(-1), oracle_mod.fp4_scales_to_128x4(gs))
+    # ... and the row-major run agrees with the oracle (sampled rows).
+    sel = _sample_rows(rows, seed) if rows > 1024 else np.arange(rows)
+    a_b, m_b = bits(inp.attn)[sel], bits(inp.mlp)[sel]
+    rp, rs, s_pre, pre = oracle_mod.token_cat_fp4(a_b, m_b, inp.fp4_g)
+    x = oracle_mod.f32_from_bf16(np.concatenate([a_b, m_b], axis=1))
+    rs_full = np.concatenate([rs[:len(sel)], np.zeros((rows_pad - rows, cols // 16), np.uint8)])
+    ec, es = check_fp4("fp4", packed.bits()[sel], np.concatenate([gs[sel], gs[rows:]]), rp,
+                       rs_full, s_pre, pre, x, inp.fp4_g, e4m3_table, oracle_mod.e2m1_encode)
     print(f"exact: codes {ec:.6f} scales {es:.6f}")
 
 
