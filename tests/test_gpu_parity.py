@@ -591,3 +591,74 @@ def test_runs_on_a_side_stream(qe):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     assert torch.equal(ref, out)
+
+
+def test_hip_graph_capture_replays_match_eager(qe):
+    """Every entry point is recorded into one HIP graph (through torch's graph
+    capture on the current stream) and replayed three times, with eager work
+    that overwrites the outputs in between; each replay must reproduce the
+    eager results bit for bit."""
+    torch.manual_seed(3)
+    H, R = 3072, 256
+    x = torch.randn(R, H, device="cuda").to(torch.bfloat16)
+    res = torch.randn(R, H, device="cuda").to(torch.bfloat16)
+    vec = lambda std, mean=0.0: (torch.randn(H, device="cuda") * std + mean).to(torch.bfloat16)
+    sc, sh, bias, gate = vec(0.1), vec(0.1), vec(0.02), vec(0.1, 1.0)
+    s8, g4 = dscalar(0.0625), dscalar(448.0)
+    inp = synth.qkv_inputs(64, 16, 24, 128, seed=4)
+    qkv_img, qkv_txt = dev(inp.img_qkv), dev(inp.txt_qkv)
+    W = inp.width
+    tabs = [torch.from_numpy(np.ascontiguousarray(t)).cuda()
+            for t in (inp.img_cos, inp.img_sin, inp.txt_cos, inp.txt_sin)]
+    ws = [dev(w) for w in (inp.img_q_w, inp.img_k_w, inp.txt_q_w, inp.txt_k_w)]
+    a, m = x[:, :1024].contiguous(), x[:, 1024:].contiguous()
+
+    outs = {
+        "y": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
+        "q": torch.empty(R, H, dtype=torch.uint8, device="cuda"),
+        "r": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
+        "y2": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
+        "q2": torch.empty(R, H, dtype=torch.uint8, device="cuda"),
+        "r4": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
+        "p4": torch.empty(R, H // 2, dtype=torch.uint8, device="cuda"),
+        "s4": torch.empty(R, H // 16, dtype=torch.uint8, device="cuda"),
+        "jq": torch.empty(80, 24, 128, dtype=torch.bfloat16, device="cuda"),
+        "jk": torch.empty(80, 24, 128, dtype=torch.bfloat16, device="cuda"),
+        "jv": torch.empty(80, 24, 128, dtype=torch.bfloat16, device="cuda"),
+        "bma": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
+        "c8": torch.empty(R, H, dtype=torch.uint8, device="cuda"),
+        "c4": torch.empty(R, H // 2, dtype=torch.uint8, device="cuda"),
+        "c4s": torch.empty(R, H // 16, dtype=torch.uint8, device="cuda"),
+    }
+
+    def run():
+        o = outs
+        qe.dit_norm_modulate_fp8(o["y"], o["q"], x, sc, sh, s8, R, H, 1e-6)
+        qe.dit_scale_residual_norm_modulate_fp8(o["r"], o["y2"], o["q2"], x, bias, gate, res, sc,
+                                                sh, s8, R, H, 1e-6)
+        qe.dit_scale_residual_norm_modulate_fp4(o["r4"], None, o["p4"], o["s4"],
+                                                qe.DIT_FP4_SCALES_128X4, x, bias, gate, res, sc,
+                                                sh, g4, R, H, 1e-6)
+        qe.dit_qkv_epilogue(o["jq"], o["jk"], o["jv"], qkv_img[:, :W], qkv_img[:, W:2 * W],
+                            qkv_img[:, 2 * W:], 64, 3 * W, qkv_txt[:, :W], qkv_txt[:, W:2 * W],
+                            qkv_txt[:, 2 * W:], 16, 3 * W, *ws, *tabs, 64, 24, 128, 1e-6, 1e-6)
+        qe.dit_bias_mul_add(o["bma"], x, bias, gate, res, R, H)
+        qe.dit_token_cat_quant(qe.DIT_QUANT_FP8_E4M3, o["c8"], None, a, 1024, m, H - 1024, R, s8)
+        qe.dit_token_cat_quant(qe.DIT_QUANT_FP4_E2M1, o["c4"], o["c4s"], a, 1024, m, H - 1024,
+                               R, g4)
+
+    run()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in outs.values():  # eager work between replays
+            v.view(torch.uint8).fill_(0xA5 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v.view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
