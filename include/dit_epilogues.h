@@ -266,7 +266,8 @@ int dit_bias_mul_add(void* y, const void* x, const void* bias, const void* gate,
  *
  *   kind      DIT_QUANT_FP8_E4M3, DIT_QUANT_FP4_E2M1 (row-major scales) or
  *             DIT_QUANT_FP4_E2M1_128X4 (scales in the 128x4 tile layout, see
- *             DIT_FP4_SCALES_128X4; a_cols + b_cols must be a multiple of 64)
+ *             DIT_FP4_SCALES_128X4; a_cols + b_cols must be a multiple of 64
+ *             and out_scales 16-byte aligned)
  *   out       FP8: [rows, a_cols + b_cols] E4M3 bytes
  *             FP4: [rows, (a_cols + b_cols) / 2] bytes, element 2k in the low
  *             nibble of byte k, element 2k+1 in the high nibble

@@ -328,6 +328,8 @@ int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales, const v
     if (kind == DIT_QUANT_FP4_E2M1_128X4 && (a_cols + b_cols) % 64 != 0)
         return fail(DIT_ERR_UNSUPPORTED, "%s: the 128x4 scale layout needs a_cols + b_cols %% 64 == 0",
                     fn);
+    if (kind == DIT_QUANT_FP4_E2M1_128X4 && out_scales && !aligned(out_scales, 16))
+        return fail(DIT_ERR_ALIGN, "%s: 128x4 scales must be 16-byte aligned", fn);
     if (!out || !a || !scale_dev || (b_cols > 0 && !b) ||
         (fp4 && !out_scales))
         return fail(DIT_ERR_NULL, "%s: a required pointer is NULL", fn);

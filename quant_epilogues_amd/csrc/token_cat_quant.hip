@@ -126,6 +126,73 @@ __global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a, in
     *scale_out = (uint8_t)s8;
 }
 
+// FP4 with the scales in 128x4 tiles. Inside a tile, the 32 rows m with the
+// same m % 32 / 8 hold one contiguous 128-byte line per tile column (4
+// groups): rows m0 + 32 i + r (i < 4, r < 8) for m0 = 128 t + 8 j. A
+// workgroup takes such a 32-row set and kTiledGroups groups: wave i computes
+// rows m0 + 32 i + r one after another (a lane per group, as in the
+// row-major kernel), stages the scale bytes in LDS, and after one barrier
+// the workgroup writes every line whole, 8 bytes per lane. Rows past `rows`
+// (up to the 128-row padding) only contribute zero scales. Needs groups % 4
+// == 0 (whole tile columns).
+constexpr int kTiledGroups = 64;
+
+__global__ __launch_bounds__(256) void token_cat_fp4_tiled_kernel(TokenCatArgs a) {
+    __shared__ uint8_t sbuf[32][kTiledGroups];  // [i * 8 + r][group in chunk]
+    const int lane = threadIdx.x & 63;
+    const int i = threadIdx.x >> 6;  // wave: rows m0 + 32 i + r
+    const int64_t cols = a.a_cols + a.b_cols;
+    const int groups = (int)(cols >> 4);
+    const int g0 = blockIdx.x * kTiledGroups;
+    const int64_t m0 = (int64_t)(blockIdx.y >> 2) * 128 + (blockIdx.y & 3) * 8;
+    const float gscale = *a.scale;  // global inverse scale
+    const int g = g0 + lane;
+    for (int r = 0; r < 8; ++r) {
+        const int64_t row = m0 + 32 * i + r;
+        uint32_t s8 = 0;
+        if (row < a.rows && g < groups) {
+            float f[16];
+            load16x2(cat_source(a, row, g), f);
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[e]));
+            const float s_pre = (amax / 6.0f) * gscale;
+            s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s_pre, 448.0f), 0.0f, 0,
+                                                           false) & 0xFFu;
+            u32x2 packed = {0u, 0u};
+            if (s8 != 0) {
+                const float kq = gscale / e4m3_value_pos(s8);  // IEEE division
+                float t0[8], t1[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    t0[e] = f[e] * kq;
+                    t1[e] = f[8 + e] * kq;
+                }
+                packed = (u32x2){pack_e2m1x8(t0), pack_e2m1x8(t1)};
+            }
+            store8(a.out + row * (cols >> 1) + 8 * g, packed);
+        }
+        sbuf[i * 8 + r][lane] = (uint8_t)s8;
+    }
+    __syncthreads();
+    // Lines: kTiledGroups / 4 tile columns x 128 bytes; lane t writes bytes
+    // 8 (t % 16) .. +7 of line t / 16. Byte p of a line is row m0 + 32 ((p % 16)
+    // / 4) + p / 16, group 4 * column + p % 4.
+    const int col = threadIdx.x >> 4;
+    const int gc = g0 + 4 * col;
+    if (gc >= groups) return;
+    const int p0 = 8 * (threadIdx.x & 15);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const int p = p0 + b;
+        const uint32_t v = sbuf[((p & 15) >> 2) * 8 + (p >> 4)][4 * col + (p & 3)];
+        w[b >> 2] |= v << (8 * (b & 3));
+    }
+    const int64_t line = ((m0 >> 7) * (groups >> 2) + (gc >> 2)) * 512 + (m0 & 31) * 16;
+    store8(a.out_scales + line + p0, (u32x2){w[0], w[1]});
+}
+
 // One workgroup per (tile, row); rows go in launches of at most kRowsPerLaunch
 // (the grid's y extent), usually one.
 constexpr int64_t kRowsPerLaunch = 65536;
@@ -158,6 +225,25 @@ hipError_t launch_token_cat_fp8(const TokenCatArgs& a, hipStream_t stream) {
 // One lane per 16-element group measured faster than two lanes per group.
 hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream) {
     const int64_t rows_padded = (a.rows + 127) / 128 * 128;
+    if (a.scales_tiled) {
+        const int64_t groups = (a.a_cols + a.b_cols) / 16;
+        const int64_t chunks = (groups + kTiledGroups - 1) / kTiledGroups;
+        for (int64_t set0 = 0; set0 < rows_padded / 32; set0 += kRowsPerLaunch) {
+            const int64_t n = rows_padded / 32 - set0 < kRowsPerLaunch ? rows_padded / 32 - set0
+                                                                       : kRowsPerLaunch;
+            TokenCatArgs b = a;  // row sets [set0, set0 + n): shift the row origin
+            b.a = a.a + set0 * 32 * a.a_cols;
+            b.b = a.b ? a.b + set0 * 32 * a.b_cols : nullptr;
+            b.out = a.out + set0 * 32 * ((a.a_cols + a.b_cols) / 2);
+            b.out_scales = a.out_scales + set0 * 32 * groups;
+            b.rows = a.rows - set0 * 32;
+            hipLaunchKernelGGL(token_cat_fp4_tiled_kernel, dim3((unsigned)chunks, (unsigned)n),
+                               dim3(256), 0, stream, b);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     return launch_rows_tiles(token_cat_fp4_kernel, a, rows_padded, kTile, (a.a_cols + a.b_cols) / 16,
                              stream);
 }

@@ -238,4 +238,5 @@ def test_token_cat_tiled_scales_need_whole_tiles(native):
     tiled = native.DIT_QUANT_FP4_E2M1_128X4
     assert f(tiled, FAKE, FAKE, FAKE, 6144, FAKE2, 16, 4, FAKE, None) == native.DIT_ERR_UNSUPPORTED
     assert f(tiled, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, 0, FAKE, None) == native.DIT_OK
+    assert f(tiled, FAKE, FAKE + 8, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_ALIGN
     assert f(3, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_UNSUPPORTED
