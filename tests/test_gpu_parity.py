@@ -78,6 +78,7 @@ def _print_case(*args):
 
 NORM_CASES = [
     (127, 3072, 0.0625, 0),   # the small Qwen-Image case
+    (512, 3072, 0.0625, 11),  # Qwen-Image text tokens, as bench.py launches them
     (1, 3072, 0.4754464328, 1),
     (1024, 3072, 0.02, 2),
     (4096, 3072, 0.5, 3),     # full image-token count
