@@ -175,19 +175,31 @@ __device__ __forceinline__ int64_t fp4_scale_offset(int64_t m, int k, int groups
 
 // ---- reciprocal square root -------------------------------------------------
 
-// RN32(1 / sqrt(v)) for v > 0 within the fp32 range: fp32 reciprocal-sqrt seed,
-// two Newton steps in binary64 (error a few binary64 ulps), one rounding to
-// fp32. It differs from the correctly rounded value only when 1/sqrt(v) lies
-// within a few binary64 ulps of an fp32 rounding boundary.
+// RN32(1 / sqrt(v)) for any v >= 0 held in binary64 (row statistics of bf16
+// data reach far beyond the fp32 range: a row holding 1e30 has a variance
+// near 1e57). v is first scaled by an even power of two into [0.5, 2) --
+// exact in binary64 -- so that the fp32 reciprocal-sqrt seed neither
+// overflows nor underflows; two Newton steps in binary64 (error a few
+// binary64 ulps) follow, the scaling is undone exactly, and the result is
+// rounded once to fp32. It differs from the correctly rounded value only when
+// 1/sqrt(v) lies within a few binary64 ulps of an fp32 rounding boundary.
 __device__ __forceinline__ float rsqrt_rn32(double v) {
-    double y = (double)__builtin_amdgcn_rsqf((float)v);
+    if (v == 0.0) return __builtin_inff();
+    if (v == __builtin_inf()) return 0.0f;
+    int e;
+    double m = __builtin_frexp(v, &e);  // v = m * 2^e, m in [0.5, 1)
+    if (e & 1) {                        // make the exponent even: m in [1, 2)
+        m *= 2.0;
+        e -= 1;
+    }
+    double y = (double)__builtin_amdgcn_rsqf((float)m);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        const double t = v * y;
-        const double e = __builtin_fma(-t, y, 1.0);  // 1 - v y^2
-        y = __builtin_fma(0.5 * y, e, y);
+        const double t = m * y;
+        const double err = __builtin_fma(-t, y, 1.0);  // 1 - m y^2
+        y = __builtin_fma(0.5 * y, err, y);
     }
-    return (float)y;
+    return (float)__builtin_ldexp(y, -(e / 2));  // 1/sqrt(v) = y * 2^(-e/2)
 }
 
 // ---- wave64 reductions --------------------------------------------------------

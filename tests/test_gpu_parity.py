@@ -663,3 +663,60 @@ def test_hip_graph_capture_replays_match_eager(qe):
         torch.cuda.synchronize()
         for k, v in outs.items():
             assert torch.equal(v.view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
+
+
+def test_degenerate_inputs(qe, oracle_mod, e4m3_table):
+    """Constant, zero and outlier rows through the norms (with FP8 saturation
+    and NVFP4), zero and huge heads through the QKV epilogue, and all-zero,
+    single-value and subnormal groups through the FP4 token concatenation."""
+    H = 3072
+    rows = np.zeros((8, H), np.float32)
+    rows[0] = 2.5                               # constant: variance 0
+    rows[2, 17] = 1e30                          # one outlier
+    rows[3] = np.where(np.arange(H) % 2, 1e-30, -1e-30)  # tiny alternating
+    rows[4] = np.linspace(-40000, 40000, H)     # wide range
+    rows[5, ::7] = 3.0                          # sparse
+    rows[6] = 1e-38                             # near the smallest normal
+    rows[7] = -7.0                              # negative constant
+    x = torch.from_numpy(rows).to(torch.bfloat16)
+    sc = torch.from_numpy(np.random.default_rng(0).standard_normal(H).astype(np.float32) * 0.1).to(torch.bfloat16)
+    sh = torch.from_numpy(np.random.default_rng(1).standard_normal(H).astype(np.float32) * 0.1).to(torch.bfloat16)
+    for input_scale in (1e-3, 0.0625):          # 1e-3: most FP8 codes saturate
+        y, q = qe.norm_modulate_fp8(dev(x), dev(sc), dev(sh), dscalar(input_scale), 1e-6)
+        ry, rq, pre = oracle_mod.norm_modulate_fp8(bits(x), bits(sc), bits(sh),
+                                                   float(np.float32(input_scale)), 1e-6)
+        check_bf16("degenerate y", y.cpu().view(torch.int16).numpy().view(np.uint16), ry)
+        check_fp8("degenerate q", q.cpu().numpy(), rq, pre, e4m3_table)
+    y4, p4, s4 = qe.norm_modulate_fp4(dev(x), dev(sc), dev(sh), dscalar(448.0), 1e-6)
+    ry, rp, rs, s_pre, pre = oracle_mod.norm_modulate_fp4(bits(x), bits(sc), bits(sh), 448.0, 1e-6)
+    check_bf16("degenerate fp4 y", y4.cpu().view(torch.int16).numpy().view(np.uint16), ry)
+    check_fp4("degenerate fp4", p4.cpu().numpy(), s4.cpu().numpy(), rp, rs, s_pre, pre,
+              oracle_mod.f32_from_bf16(ry), 448.0, e4m3_table, oracle_mod.e2m1_encode)
+
+    # QKV: head 0 of every token all zero (mean square 0), head 1 huge.
+    inp = synth.qkv_inputs(6, 2, 4, 128, seed=7)
+    for packed in (inp.img_qkv, inp.txt_qkv):
+        v = packed.float()
+        v[:, 0:128] = 0.0
+        v[:, 128:256] *= 1e30
+        v[:, 512:640] = 0.0        # K head 0
+        packed.copy_(v.to(torch.bfloat16))
+    gq, gk, gv = _run_qkv(qe, inp)
+    rq, rk, rv = _oracle_qkv(oracle_mod, inp)
+    check_bf16("degenerate joint_q", gq, rq)
+    check_bf16("degenerate joint_k", gk, rk)
+    check_exact("degenerate joint_v", gv, rv)
+
+    # FP4 groups: all zero, one non-zero value, subnormal bf16 values.
+    cols = 64
+    g = np.zeros((4, cols), np.float32)
+    g[0, 16 + 5] = -3.0
+    g[1, :16] = 1e-39                       # bf16 subnormals
+    g[2, 32:48] = np.arange(16) * 0.25
+    g[3] = 6.0
+    gb = torch.from_numpy(g).to(torch.bfloat16)
+    for gv_ in (1.0, 448.0):
+        pk, scs = qe.token_cat_quant(qe.DIT_QUANT_FP4_E2M1, dev(gb), None, dscalar(gv_))
+        rp, rs, s_pre, pre = oracle_mod.token_cat_fp4(bits(gb), np.zeros((4, 0), np.uint16), gv_)
+        check_fp4("degenerate groups", pk.cpu().numpy(), scs.cpu().numpy(), rp, rs, s_pre, pre,
+                  oracle_mod.f32_from_bf16(bits(gb)), gv_, e4m3_table, oracle_mod.e2m1_encode)
