@@ -387,6 +387,20 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_each_way": nbytes, "copies": reps}), flush=True)
 
 
+def extra_timings(torch, qe, steps):
+    """Isolated per-launch timings of the kernels timed beside the step."""
+    ex = Workload(torch, qe, seed=0, names=Workload.EXTRA)
+    _, ext = kernel_timings(torch, qe, ex, steps, in_step=False)
+    extra = {}
+    for name, nbytes, _ in ex.launches:
+        iso = ext[name]["iso_ms"]
+        extra[name] = {"us_per_call": round(1e3 * iso, 3), "bytes": nbytes,
+                       "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
+                       "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                       "rotation_sets": ext[name]["sets"]}
+    return extra
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +416,8 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the kernels timed beside the step (FLUX.2 QKV, output selections)")
+    ap.add_argument("--extra-only", action="store_true",
+                    help="time only the kernels timed beside the step, each in isolation")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only, no per-kernel timing (for counter runs)")
     ap.add_argument("--blocks", type=int, default=0,
@@ -424,6 +440,10 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
+    if args.extra_only:
+        print(json.dumps({"metric": METRIC, "extra_kernels": extra_timings(torch, qe, args.steps)}),
+              flush=True)
+        return
     names = tuple(args.only.split(",")) if args.only else Workload.ALL
     wl = Workload(torch, qe, seed=0, names=names)
     for _ in range(args.warmup):
@@ -444,17 +464,7 @@ def main():
                          "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
                          "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                          "us_in_step": round(1e3 * marg, 3), "rotation_sets": t["sets"]}
-    extra = {}
-    if not args.only and not args.no_extra:
-        ex = Workload(torch, qe, seed=0, names=Workload.EXTRA)
-        _, ext = kernel_timings(torch, qe, ex, args.steps, in_step=False)
-        for name, nbytes, _ in ex.launches:
-            iso = ext[name]["iso_ms"]
-            extra[name] = {"us_per_call": round(1e3 * iso, 3), "bytes": nbytes,
-                           "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
-                           "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                           "rotation_sets": ext[name]["sets"]}
-        del ex
+    extra = {} if args.only or args.no_extra else extra_timings(torch, qe, args.steps)
     dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
     achieved = kernels[dom]["gb_s"]
     traffic = profiled_traffic(dom)
