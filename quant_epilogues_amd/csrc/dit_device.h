@@ -50,6 +50,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// bf16(v) (round to nearest even) as the fp32 value it denotes, in one
+// conversion: packing (0, v) leaves bf16(v) in the high half over a zero low
+// half, which is exactly the fp32 bit pattern of that bf16 value.
+__device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pack_bf16(0.0f, v)); }
+
+// Two fp32 values that are already bf16 values -> one word of two bf16 (a in
+// the low half): their high halves, gathered with one byte permute.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
 // 8 bf16 held in 16 bytes <-> 8 floats.
 __device__ __forceinline__ void unpack8(const u32x4& v, float (&f)[8]) {
     f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
@@ -140,8 +151,11 @@ __device__ __forceinline__ float clamp_e4m3(float v) {
 }
 
 // Four values already clamped to [-448, 448] -> four E4M3 bytes (a lowest).
+// The first conversion writes the low half and keeps the high half of its
+// third operand, which the second conversion then overwrites: any register
+// will do there, so `a`'s own bits are passed instead of a zeroed one.
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -204,12 +218,15 @@ __device__ __forceinline__ float rsqrt_rn32(double v) {
 
 // ---- wave64 reductions --------------------------------------------------------
 
-// DPP move of a 64-bit value (both halves with the same lane pattern).
+// DPP move of a 64-bit value (both halves with the same lane pattern). The
+// patterns used here (quad permutes, row mirrors) read a lane of the same
+// 16-lane row for every lane, and all rows and banks are enabled, so every
+// lane is written and no prior destination value is needed.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
     const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
 }
 

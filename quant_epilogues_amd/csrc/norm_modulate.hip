@@ -62,21 +62,27 @@ __device__ __forceinline__ void col8(const float* cols, const NormModulateArgs& 
     }
 }
 
-template <int MODE, int WPR, int RPW, int V, bool kLds, bool kFp4>
+// kExact (plain variant only): hidden == 512 WPR V, so every chunk index lies
+// inside the row and no load needs a predicate; a wave past the last row then
+// reads the last row again (its results are dropped) instead of zero-filling
+// its registers. For the residual variants the predicated form measured
+// faster on MI355X and is kept.
+template <int MODE, int WPR, int RPW, int V, bool kLds, bool kFp4, bool kExact>
 __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormModulateArgs a,
                                                                             double inv_hidden) {
     // cols: [kColVecs][hidden] fp32 = 1 + scale, shift, gate, bias
     extern __shared__ float cols[];
     __shared__ double scratch[RPW][WPR][2];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rw = wave / WPR;  // row slot in the workgroup
     const int sw = wave % WPR;  // wave within the row
     const int64_t row = (int64_t)blockIdx.x * RPW + rw;
-    const bool active = row < a.rows;  // every wave still reaches the barriers
+    const bool active = row < a.rows;  // wave-uniform; every wave still reaches the barriers
     const int H = a.hidden;
     const int cpr = H >> 3;  // chunks per row
     const int64_t base = row * H;
+    const int64_t lbase = (kExact && !active ? a.rows - 1 : row) * H;  // rows >= 1 here
 
     // 1. Streaming loads of this wave's chunks.
     u32x4 xin[V], rin[V];
@@ -84,19 +90,27 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
 #pragma unroll
     for (int k = 0; k < V; ++k) {
         const int c = 64 * (sw + WPR * k) + lane;
-        ok[k] = active && c < cpr;
-        xin[k] = ok[k] ? stream_load16(a.x + base + 8 * c) : (u32x4){0, 0, 0, 0};
-        if (MODE != kPlain) rin[k] = ok[k] ? stream_load16(a.residual + base + 8 * c) : (u32x4){0, 0, 0, 0};
+        ok[k] = active && (kExact || c < cpr);
+        if (kExact) {
+            xin[k] = stream_load16(a.x + lbase + 8 * c);
+            if (MODE != kPlain) rin[k] = stream_load16(a.residual + lbase + 8 * c);
+        } else {
+            xin[k] = ok[k] ? stream_load16(a.x + base + 8 * c) : (u32x4){0, 0, 0, 0};
+            if (MODE != kPlain)
+                rin[k] = ok[k] ? stream_load16(a.residual + base + 8 * c) : (u32x4){0, 0, 0, 0};
+        }
     }
 
     const bool want_y = a.y != nullptr, want_q = a.q != nullptr;  // wave-uniform
     const float inv = want_q ? 1.0f / *a.input_scale : 0.0f;  // IEEE division
     const float g4 = kFp4 ? *a.input_scale : 0.0f;  // FP4: the global inverse scale
 
-    // 2. Column vectors to fp32 in LDS, while the streaming loads are in flight.
+    // 2. Column vectors to fp32 in LDS, while the streaming loads are in
+    // flight; one vector at a time, which keeps the kernel's register peak
+    // (and so its occupancy) where the streaming loads alone put it.
     if (kLds) {
         for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
-#pragma unroll
+#pragma unroll 1
             for (int which = 0; which < kColVecs<MODE>; ++which) {
                 float f[8];
                 col8<false>(cols, a, which, c, f);
@@ -118,9 +132,9 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
         float xf[8], rf[8], gf[8];
         unpack8(xin[k], xf);
         unpack8(rin[k], rf);
-        if (ok[k]) col8<kLds>(cols, a, 2, c, gf);
+        if (kExact || ok[k]) col8<kLds>(cols, a, 2, c, gf);
         else for (int i = 0; i < 8; ++i) gf[i] = 0.0f;
-        if (MODE == kBiasResidual && ok[k]) {
+        if (MODE == kBiasResidual && (kExact || ok[k])) {
             float bf[8];
             col8<kLds>(cols, a, 3, c, bf);
 #pragma unroll
@@ -209,27 +223,26 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
 #pragma unroll
             for (int i = 0; i < 8; ++i) ops[i] = sh[i] = 0.0f;
         }
-        uint32_t yw[4];
-        float yv[8];
+        // m = norm * (1 + scale) + shift in fp32, from the bf16 norm.
+        float m[8];
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            const float t0 = (v[k][i] - mean32) * factor;
-            const float t1 = (v[k][i + 1] - mean32) * factor;
-            const uint32_t nw = pack_bf16(t0, t1);  // normalised row, bf16
-            const float m0 = __builtin_fmaf(bf_lo(nw), ops[i], sh[i]);
-            const float m1 = __builtin_fmaf(bf_hi(nw), ops[i + 1], sh[i + 1]);
-            yw[i / 2] = pack_bf16(m0, m1);
-            yv[i] = bf_lo(yw[i / 2]);
-            yv[i + 1] = bf_hi(yw[i / 2]);
+        for (int i = 0; i < 8; ++i) {
+            const float norm = round_bf16((v[k][i] - mean32) * factor);
+            m[i] = __builtin_fmaf(norm, ops[i], sh[i]);
         }
+        // y = bf16(m): packed for the store, and as fp32 values (each from one
+        // conversion) when a quantised output is formed from it.
         if constexpr (kFp4) {
+            float yv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yv[i] = round_bf16(m[i]);
             // 16-element group = this lane's 8 values and its neighbour's
             // (lanes 2g and 2g + 1 hold chunks 2g and 2g + 1 of the row).
             float amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(yv[i]));
             const float other = __builtin_bit_cast(
-                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false));
+                float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false));
             amax = __builtin_fmaxf(amax, other);  // quad_perm [1, 0, 3, 2]
             const float s_pre = (amax / 6.0f) * g4;
             const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
@@ -243,20 +256,30 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
                 packed = pack_e2m1x8(t);
             }
             if (ok[k]) {
-                if (want_y) store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
+                if (want_y)
+                    store16(a.y + base + 8 * c,
+                            (u32x4){pack_bf16_exact(yv[0], yv[1]), pack_bf16_exact(yv[2], yv[3]),
+                                    pack_bf16_exact(yv[4], yv[5]), pack_bf16_exact(yv[6], yv[7])});
                 store4(a.fp4 + row * (H >> 1) + 4 * c, packed);
                 if ((lane & 1) == 0)
                     a.fp4_scales[fp4_scale_offset(row, c >> 1, H >> 4, a.fp4_tiled)] = (uint8_t)s8;
             }
-            continue;
-        }
-        if (want_y) store16(a.y + base + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});
-        if (want_q) {  // from the bf16 y, stored or not
+        } else if (want_q) {  // q from the bf16 y, stored or not
+            float yv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yv[i] = round_bf16(m[i]);
+            if (want_y)
+                store16(a.y + base + 8 * c,
+                        (u32x4){pack_bf16_exact(yv[0], yv[1]), pack_bf16_exact(yv[2], yv[3]),
+                                pack_bf16_exact(yv[4], yv[5]), pack_bf16_exact(yv[6], yv[7])});
             const uint32_t q0 = pack_e4m3x4(clamp_e4m3(yv[0] * inv), clamp_e4m3(yv[1] * inv),
                                             clamp_e4m3(yv[2] * inv), clamp_e4m3(yv[3] * inv));
             const uint32_t q1 = pack_e4m3x4(clamp_e4m3(yv[4] * inv), clamp_e4m3(yv[5] * inv),
                                             clamp_e4m3(yv[6] * inv), clamp_e4m3(yv[7] * inv));
             store8(a.q + base + 8 * c, (u32x2){q0, q1});
+        } else {  // y only
+            store16(a.y + base + 8 * c, (u32x4){pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]),
+                                                pack_bf16(m[4], m[5]), pack_bf16(m[6], m[7])});
         }
     }
 }
@@ -269,9 +292,13 @@ hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
     const uint64_t blocks = (uint64_t)((grid_rows + RPW - 1) / RPW);
     if (blocks * (64 * WPR * RPW) >= kMaxGridLanes) return kGridTooLarge;
     const size_t lds = kLds ? (size_t)kColVecs<MODE> * a.hidden * sizeof(float) : 0;
-    hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4>),
-                       dim3((unsigned)blocks), dim3(64 * WPR * RPW), lds, stream, a,
-                       1.0 / (double)a.hidden);
+    const dim3 grid((unsigned)blocks), block(64 * WPR * RPW);
+    if (MODE == kPlain && a.hidden == 512 * WPR * V)
+        hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4, true>), grid,
+                           block, lds, stream, a, 1.0 / (double)a.hidden);
+    else
+        hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4, false>), grid,
+                           block, lds, stream, a, 1.0 / (double)a.hidden);
     return hipGetLastError();
 }
 
