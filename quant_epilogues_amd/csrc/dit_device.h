@@ -116,34 +116,6 @@ __device__ __forceinline__ void pack8_exact_sum(const float (&p)[8], const float
     }
 }
 
-// bf16 (round to nearest even) of 8 binary64 values, two per word, via fp32:
-// RN32 cannot move a value across a bf16 midpoint, only onto one, and that
-// rare case is settled by comparing with the binary64 value (one wave-uniform
-// branch, almost never taken).
-__device__ __forceinline__ void pack8_from_f64(const double (&d)[8], uint32_t (&w)[4]) {
-    float f[8];
-    bool tie = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        f[i] = (float)d[i];
-        tie |= (__float_as_uint(f[i]) & 0xFFFFu) == 0x8000u;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = pack_bf16(f[2 * j], f[2 * j + 1]);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tie) != 0, 0)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t u = __float_as_uint(f[i]);
-            if ((u & 0xFFFFu) != 0x8000u) continue;
-            const double back = (double)f[i];
-            if (d[i] == back) continue;
-            const uint32_t h = (u >> 16) + (__builtin_fabs(d[i]) > __builtin_fabs(back) ? 1u : 0u);
-            const int sh = (i & 1) * 16;
-            w[i / 2] = (w[i / 2] & ~(0xFFFFu << sh)) | (h << sh);
-        }
-    }
-}
-
 // ---- FP8 E4M3FN ------------------------------------------------------------
 
 __device__ __forceinline__ float clamp_e4m3(float v) {

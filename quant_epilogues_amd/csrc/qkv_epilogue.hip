@@ -25,6 +25,51 @@
 namespace dit {
 namespace {
 
+// bf16 bits (round to nearest even) of the binary64 value d, given its fp32
+// rounding f, when f lies exactly on a bf16 midpoint: RN32 cannot carry a
+// value across a midpoint, only onto one, so d decides the side and an exact
+// tie keeps the even neighbour.
+__device__ __forceinline__ uint32_t bf16_of_midpoint(float f, double d) {
+    const uint32_t t = __float_as_uint(f) >> 16;  // f truncated to bf16 (toward zero)
+    if (d == (double)f) return t + (t & 1u);      // exact tie: the even neighbour
+    return t + (__builtin_fabs(d) > __builtin_fabs((double)f) ? 1u : 0u);
+}
+
+// Interleaved RoPE of one lane's 8 normalised values (pairs (2q, 2q + 1)),
+// each output one binary64 fma of exact products (a bf16 value times an fp32
+// table entry), rounded to bf16 through fp32. A value whose fp32 rounding
+// sits on a bf16 midpoint (one wave-uniform branch, almost never taken) is
+// recomputed and settled from binary64, so no binary64 value has to outlive
+// its conversion.
+__device__ __forceinline__ void rope_pack8(const float (&n)[8], const float (&cs)[4],
+                                           const float (&sn)[4], uint32_t (&w)[4]) {
+    bool tie = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const double n0 = (double)n[2 * q], n1 = (double)n[2 * q + 1];
+        const double c = (double)cs[q], sv = (double)sn[q];
+        const float f0 = (float)__builtin_fma(n0, c, -(n1 * sv));
+        const float f1 = (float)__builtin_fma(n1, c, n0 * sv);
+        tie |= (__float_as_uint(f0) & 0xFFFFu) == 0x8000u;
+        tie |= (__float_as_uint(f1) & 0xFFFFu) == 0x8000u;
+        w[q] = pack_bf16(f0, f1);
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tie) != 0, 0)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double n0 = (double)n[2 * q], n1 = (double)n[2 * q + 1];
+            const double c = (double)cs[q], sv = (double)sn[q];
+            const double d0 = __builtin_fma(n0, c, -(n1 * sv));
+            const double d1 = __builtin_fma(n1, c, n0 * sv);
+            const float f0 = (float)d0, f1 = (float)d1;
+            if ((__float_as_uint(f0) & 0xFFFFu) == 0x8000u)
+                w[q] = (w[q] & 0xFFFF0000u) | bf16_of_midpoint(f0, d0);
+            if ((__float_as_uint(f1) & 0xFFFFu) == 0x8000u)
+                w[q] = (w[q] & 0x0000FFFFu) | (bf16_of_midpoint(f1, d1) << 16);
+        }
+    }
+}
+
 // kPasses 4-head passes per wave (a wave covers 4 * kPasses heads); a token
 // has kHBlocks such head groups. Grid: x = group of 4 units, y = part; unit
 // u of a part is head group u % kHBlocks of joint token u / kHBlocks, so
@@ -77,8 +122,8 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a) {
     const float* sin_row = (is_txt ? a.txt_sin : a.img_sin) + i * a.rope_stride + 4 * s;
     const float4 c4 = *reinterpret_cast<const float4*>(cos_row);
     const float4 s4 = *reinterpret_cast<const float4*>(sin_row);
-    const double cs[4] = {c4.x, c4.y, c4.z, c4.w};
-    const double sn[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float cs[4] = {c4.x, c4.y, c4.z, c4.w};
+    const float sn[4] = {s4.x, s4.y, s4.z, s4.w};
     const double eps = (double)(is_txt ? a.txt_eps : a.img_eps);
 
 #pragma unroll
@@ -94,24 +139,11 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvArgs a) {
         ss = row16_sum(ss);
         const float inv = rsqrt_rn32(ss * (1.0 / kHeadDim) + eps);
 
-        float n[8];
+        float n[8];  // the normalised head, rounded to bf16
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const uint32_t nw = pack_bf16((x[e] * inv) * w[e], (x[e + 1] * inv) * w[e + 1]);
-            n[e] = bf_lo(nw);
-            n[e + 1] = bf_hi(nw);
-        }
-        double o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const double n0 = (double)n[2 * q];
-            const double n1 = (double)n[2 * q + 1];
-            // bf16 x fp32 products are exact in binary64: one rounding each.
-            o[2 * q] = __builtin_fma(n0, cs[q], -(n1 * sn[q]));
-            o[2 * q + 1] = __builtin_fma(n1, cs[q], n0 * sn[q]);
-        }
+        for (int e = 0; e < 8; ++e) n[e] = round_bf16((x[e] * inv) * w[e]);
         uint32_t ow[4];
-        pack8_from_f64(o, ow);
+        rope_pack8(n, cs, sn, ow);
         if (head[p] < a.heads)
             store16(dst + head[p] * kHeadDim + 8 * s, (u32x4){ow[0], ow[1], ow[2], ow[3]});
     }
