@@ -38,6 +38,7 @@ METRIC = "fused-epilogue HBM GB/s (% of MI355X peak) + µs/call at Qwen-Image sh
 QWEN_HIDDEN, IMG, TXT, HEADS, HEAD_DIM = 3072, 4096, 512, 24, 128
 FLUX_ROWS, FLUX_A, FLUX_B = 4608, 6144, 18432
 FLUX_HEADS = 48  # FLUX.2: hidden 6144 = 48 heads x 128
+NORM_ROWS = (127, 128, 1024)  # LN + FP8 row counts timed beside the step (4096 is in it)
 
 
 def log(*a):
@@ -206,6 +207,8 @@ class Workload:
             "sr_norm_fp4": sr_norm_fp4,
             "cat_fp4_128x4": lambda: cat(qe.DIT_QUANT_FP4_E2M1_128X4),
         }
+        for r in NORM_ROWS:  # the plain norm at other row counts
+            builders["norm_r%d" % r] = lambda r=r: norm(r)
         self.launches = []  # (name, compulsory bytes, launch)
         for n in names:
             nbytes, fn = builders[n]()
@@ -387,6 +390,108 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_each_way": nbytes, "copies": reps}), flush=True)
 
 
+def norm_rows_timings(torch, qe, steps):
+    """The plain LN + modulation + FP8 norm (hidden 3072, bf16 y and FP8 q) at
+    127, 128 and 1024 rows: per call with rotating buffers (cold, as every
+    other launch), and on one buffer set launched back to back (warm), the
+    latency figure for the 127-row case."""
+    wl = Workload(torch, qe, seed=0, names=tuple("norm_r%d" % r for r in NORM_ROWS))
+    _, t = kernel_timings(torch, qe, wl, steps, in_step=False)
+    out = {}
+    for (name, nbytes, fn), rows in zip(wl.launches, NORM_ROWS):
+        iso = t[name]["iso_ms"]
+        warm, _ = time_launches(torch, [fn], max(steps, 100))
+        out[str(rows)] = {"us_per_call": round(1e3 * iso, 3), "warm_us_per_call": round(1e3 * warm, 3),
+                          "bytes": nbytes, "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
+                          "rotation_sets": t[name]["sets"]}
+    return out
+
+
+def split_path_timings(torch, steps):
+    """The unfused equivalents written as plain PyTorch GPU ops (separate
+    norm, modulation and quantisation kernels with materialised bf16
+    intermediates), timed like the fused launches with rotating inputs. For
+    context only: the library never runs them, and their results are not
+    checked. FP4 has no plain PyTorch form and is left out."""
+    import torch.nn.functional as F
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    bf16, fp8 = torch.bfloat16, torch.float8_e4m3fn
+    H, W = QWEN_HIDDEN, HEADS * HEAD_DIM
+
+    def randn(*shape, std=1.0, mean=0.0):
+        return (torch.randn(*shape, generator=g, device=dev) * std + mean).to(bf16)
+
+    def quant(y, inv):
+        return (y.float() * inv).clamp_(-448.0, 448.0).to(fp8)
+
+    def mk_norm():
+        x, sc, sh = randn(IMG, H), randn(H, std=0.1), randn(H, std=0.1)
+        return lambda: quant(F.layer_norm(x, (H,), eps=1e-6) * (1 + sc) + sh, 16.0)
+
+    def mk_sr():
+        x, res = randn(IMG, H), randn(IMG, H)
+        b, gt, sc, sh = randn(H, std=0.02), randn(H, std=0.1, mean=1.0), randn(H, std=0.1), randn(H, std=0.1)
+
+        def run():
+            r = res + gt * (x + b)
+            return r, quant(F.layer_norm(r, (H,), eps=1e-6) * (1 + sc) + sh, 16.0)
+        return run
+
+    def mk_qkv():
+        img, txt = randn(IMG, 3 * W), randn(TXT, 3 * W)
+        ws = [randn(HEAD_DIM, std=0.05, mean=1.0) for _ in range(4)]
+        tabs = [torch.rand(n, HEAD_DIM // 2, generator=g, device=dev) for n in (IMG, IMG, TXT, TXT)]
+
+        def stream(packed, wq, wk, c, s):
+            outs = []
+            for part, w in ((0, wq), (1, wk)):
+                t = packed[:, part * W:(part + 1) * W].unflatten(-1, (HEADS, HEAD_DIM))
+                n = (F.rms_norm(t.float(), (HEAD_DIM,), eps=1e-6) * w.float()).to(bf16)
+                p = n.float().unflatten(-1, (HEAD_DIM // 2, 2))
+                cc, ss = c[:, None, :], s[:, None, :]
+                o = torch.stack((p[..., 0] * cc - p[..., 1] * ss, p[..., 1] * cc + p[..., 0] * ss), -1)
+                outs.append(o.flatten(-2).to(bf16))
+            outs.append(packed[:, 2 * W:].unflatten(-1, (HEADS, HEAD_DIM)))
+            return outs
+
+        def run():
+            ti = stream(txt, ws[2], ws[3], tabs[2], tabs[3])
+            ii = stream(img, ws[0], ws[1], tabs[0], tabs[1])
+            return [torch.cat([t, i], 0) for t, i in zip(ti, ii)]
+        return run
+
+    def mk_bma():
+        x, res = randn(IMG + TXT, H), randn(IMG + TXT, H)
+        b, gt = randn(H, std=0.02), randn(H, std=0.5)
+        return lambda: (x + b) * gt + res
+
+    def mk_cat_fp8():
+        a, m = randn(FLUX_ROWS, FLUX_A), randn(FLUX_ROWS, FLUX_B)
+        return lambda: quant(torch.cat([a, m], 1), 20.0)
+
+    pipelines = {"norm_img": (mk_norm, bytes_norm(IMG, H)), "sr_norm": (mk_sr, bytes_sr(IMG, H)),
+                 "qkv": (mk_qkv, bytes_qkv(IMG + TXT, HEADS, HEAD_DIM)),
+                 "bma": (mk_bma, bytes_bma(IMG + TXT, H)),
+                 "cat_fp8": (mk_cat_fp8, bytes_cat_fp8(FLUX_ROWS, FLUX_A + FLUX_B))}
+    out = {}
+    for name, (mk, nbytes) in pipelines.items():
+        try:
+            sets = [mk() for _ in range(-(-ROTATION_BYTES // nbytes))]
+            for f in sets:
+                f()
+            ms, _ = time_launches(torch, sets, max(50, 2 * len(sets)))
+            out[name] = {"us_per_call": round(1e3 * ms, 3),
+                         "gb_s_of_fused_bytes": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            del sets
+        except (RuntimeError, TypeError) as e:  # a dtype or op this PyTorch build lacks
+            out[name] = {"error": str(e)[:200]}
+    torch.cuda.empty_cache()
+    return out
+
+
 def extra_timings(torch, qe, steps):
     """Isolated per-launch timings of the kernels timed beside the step."""
     ex = Workload(torch, qe, seed=0, names=Workload.EXTRA)
@@ -418,6 +523,8 @@ def main():
                     help="skip the kernels timed beside the step (FLUX.2 QKV, output selections)")
     ap.add_argument("--extra-only", action="store_true",
                     help="time only the kernels timed beside the step, each in isolation")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the PyTorch split-path timings")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only, no per-kernel timing (for counter runs)")
     ap.add_argument("--blocks", type=int, default=0,
@@ -465,6 +572,15 @@ def main():
                          "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                          "us_in_step": round(1e3 * marg, 3), "rotation_sets": t["sets"]}
     extra = {} if args.only or args.no_extra else extra_timings(torch, qe, args.steps)
+    norm_rows = {} if args.only or args.no_extra else norm_rows_timings(torch, qe, args.steps)
+    split = {}
+    if not args.only and not args.no_split:
+        log("timing the PyTorch split path ...")
+        split = split_path_timings(torch, args.steps)
+        for name, rec in split.items():
+            if "us_per_call" in rec:
+                rec["fused_us_per_call"] = kernels[name]["us_per_call"]
+                rec["fused_speedup"] = round(rec["us_per_call"] / kernels[name]["us_per_call"], 2)
     dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
     achieved = kernels[dom]["gb_s"]
     traffic = profiled_traffic(dom)
@@ -482,6 +598,8 @@ def main():
         "wall_ms_per_step": round(1e3 * wall, 4),
         "kernels": kernels,
         "extra_kernels": extra,
+        "norm_rows": norm_rows,
+        "split_path": split,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": kernels[dom]["bytes"]},
