@@ -314,8 +314,23 @@ def profiled_traffic(name):
     return rec["hbm_bytes"]
 
 
-def cpu_baseline(sample_div=2):
-    """The CPU oracle, single-threaded, on a row sample of the same step."""
+def cpu_threads():
+    """Host threads for the all-core oracle run: the cores this process may
+    use, at most 16 (a one-GPU share of the GPU host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(sample_div=2, threads=1):
+    """The CPU oracle on a row sample of the same step: single-threaded, or
+    (threads > 1) with every epilogue's rows cut into `threads` slices that
+    run on a thread pool. The oracle is called as it stands; its C entry
+    points release the GIL, so the slices run in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
@@ -332,29 +347,51 @@ def cpu_baseline(sample_div=2):
     sr = synth.scale_residual_inputs(img, H, seed=3)
     bm = synth.bias_mul_add_inputs(img + txt, H, seed=4)
     tc = synth.token_cat_inputs(flux, FLUX_A, FLUX_B, seed=5)
-    args = dict(
-        nm_i=(b(nm_i.x), b(nm_i.scale), b(nm_i.shift)), nm_t=(b(nm_t.x), b(nm_t.scale), b(nm_t.shift)),
-        qk=(b(qk.img_qkv), b(qk.txt_qkv), b(qk.img_q_w), b(qk.img_k_w), b(qk.txt_q_w), b(qk.txt_k_w)),
-        sr=(b(sr.x), b(sr.bias), b(sr.gate), b(sr.residual), b(sr.scale), b(sr.shift)),
-        bm=(b(bm.x), b(bm.bias), b(bm.gate), b(bm.residual)), tc=(b(tc.attn), b(tc.mlp)))
+    x_i, x_t = b(nm_i.x), b(nm_t.x)
+    qi, qt = b(qk.img_qkv), b(qk.txt_qkv)
+    qw = (b(qk.img_q_w), b(qk.img_k_w), b(qk.txt_q_w), b(qk.txt_k_w))
+    srx, srr = b(sr.x), b(sr.residual)
+    bmx, bmr = b(bm.x), b(bm.residual)
+    ta, tm = b(tc.attn), b(tc.mlp)
+
+    def cuts(n):  # `threads` contiguous row ranges covering [0, n)
+        return [(n * k // threads, n * (k + 1) // threads) for k in range(threads)]
+
+    tasks = []
+    for lo, hi in cuts(img):
+        tasks.append(lambda lo=lo, hi=hi: oracle.norm_modulate_fp8(
+            x_i[lo:hi], b(nm_i.scale), b(nm_i.shift), 0.0625, 1e-6))
+        tasks.append(lambda lo=lo, hi=hi: oracle.scale_residual_norm_modulate_fp8(
+            srx[lo:hi], b(sr.bias), b(sr.gate), srr[lo:hi], b(sr.scale), b(sr.shift), 0.0625, 1e-6))
+    for lo, hi in cuts(txt):
+        tasks.append(lambda lo=lo, hi=hi: oracle.norm_modulate_fp8(
+            x_t[lo:hi], b(nm_t.scale), b(nm_t.shift), 0.0625, 1e-6))
+    for (ilo, ihi), (tlo, thi) in zip(cuts(img), cuts(txt)):
+        tasks.append(lambda ilo=ilo, ihi=ihi, tlo=tlo, thi=thi: oracle.qkv_epilogue_packed(
+            qi[ilo:ihi], qt[tlo:thi], *qw, qk.img_cos[ilo:ihi], qk.img_sin[ilo:ihi],
+            qk.txt_cos[tlo:thi], qk.txt_sin[tlo:thi], HEADS, HEAD_DIM, 1e-6, 1e-6))
+    for lo, hi in cuts(img + txt):
+        tasks.append(lambda lo=lo, hi=hi: oracle.bias_mul_add(
+            bmx[lo:hi], b(bm.bias), b(bm.gate), bmr[lo:hi]))
+    for lo, hi in cuts(flux):
+        tasks.append(lambda lo=lo, hi=hi: oracle.token_cat_fp8(ta[lo:hi], tm[lo:hi], 0.05))
+        tasks.append(lambda lo=lo, hi=hi: oracle.token_cat_fp4(ta[lo:hi], tm[lo:hi], tc.fp4_g))
     t0 = time.perf_counter()
-    oracle.norm_modulate_fp8(*args["nm_i"], 0.0625, 1e-6)
-    oracle.norm_modulate_fp8(*args["nm_t"], 0.0625, 1e-6)
-    oracle.qkv_epilogue_packed(*args["qk"], qk.img_cos, qk.img_sin, qk.txt_cos, qk.txt_sin,
-                               HEADS, HEAD_DIM, 1e-6, 1e-6)
-    oracle.scale_residual_norm_modulate_fp8(*args["sr"], 0.0625, 1e-6)
-    oracle.bias_mul_add(*args["bm"])
-    oracle.token_cat_fp8(*args["tc"], 0.05)
-    oracle.token_cat_fp4(*args["tc"], tc.fp4_g)
+    if threads == 1:
+        for f in tasks:
+            f()
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda f: f(), tasks))
     secs = time.perf_counter() - t0
     C = FLUX_A + FLUX_B
     nbytes = (bytes_norm(img, H) + bytes_norm(txt, H) + bytes_qkv(img + txt, HEADS, HEAD_DIM)
               + bytes_sr(img, H) + bytes_bma(img + txt, H) + bytes_cat_fp8(flux, C)
               + bytes_cat_fp4(flux, C))
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    how = "single thread" if threads == 1 else f"{threads} threads, rows cut into {threads} slices"
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"every epilogue of the step on 1/{sample_div} of its rows "
-                      f"({img} image + {txt} text tokens, {flux} FLUX.2 rows), single thread, "
-                      f"{secs:.1f} s"}
+                      f"({img} image + {txt} text tokens, {flux} FLUX.2 rows), {how}, {secs:.1f} s"}
 
 
 def block_sequence(torch, qe, blocks, reps):
@@ -612,6 +649,7 @@ def main():
     if not args.no_cpu:
         log("timing the CPU oracle on a row sample ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_div)
+        out["cpu_baseline_all_cores"] = cpu_baseline(args.cpu_sample_div, cpu_threads())
     print(json.dumps(out), flush=True)
 
 
