@@ -567,8 +567,8 @@ def main():
                     help="skip the PyTorch split-path timings")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only, no per-kernel timing (for counter runs)")
-    ap.add_argument("--blocks", type=int, default=0,
-                    help="also time a Qwen-Image block sequence of this many blocks (e.g. 60)")
+    ap.add_argument("--blocks", type=int, default=60,
+                    help="also time a Qwen-Image block sequence of this many blocks (0: skip)")
     args = ap.parse_args()
     if args.print_source_hashes:
         print(json.dumps({n: kernel_source_hash(n) for n in KERNEL_SOURCES}))
