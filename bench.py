@@ -427,6 +427,38 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_each_way": nbytes, "copies": reps}), flush=True)
 
 
+def graph_us_per_call(torch, qe, name, nbytes, warm=False):
+    """Mean GPU time per launch of `name` with no host launch cost in the
+    way: the launches (cycling through rotating buffer sets whose total
+    exceeds twice the Infinity Cache, or one set if `warm`) are captured
+    once into a HIP graph on a side stream and the graph is replayed."""
+    s = torch.cuda.Stream()
+    nsets = 1 if warm else -(-ROTATION_BYTES // nbytes)
+    with torch.cuda.stream(s):  # the launches bind the stream current at construction
+        sets = [Workload(torch, qe, seed=2000 + i, names=(name,)) for i in range(nsets)]
+        fns = [w.launches[0][2] for w in sets]
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    calls = max(200, 2 * nsets)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(calls):
+            fns[i % nsets]()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g.replay()  # untimed first replay
+        start.record()
+        for _ in range(3):
+            g.replay()
+        end.record()
+    torch.cuda.synchronize()
+    us = 1e3 * start.elapsed_time(end) / (3 * calls)
+    del g, sets, fns
+    return us
+
+
 def norm_rows_timings(torch, qe, steps):
     """The plain LN + modulation + FP8 norm (hidden 3072, bf16 y and FP8 q) at
     127, 128 and 1024 rows: per call with rotating buffers (cold, as every
@@ -439,10 +471,14 @@ def norm_rows_timings(torch, qe, steps):
         iso = t[name]["iso_ms"]
         warm, host = time_launches(torch, [fn], max(steps, 100))
         # host_us_per_call near warm_us_per_call: the loop is bound by the
-        # launch calls, and the kernel itself is shorter than reported.
+        # launch calls; the graph-replayed figures are the kernel's own.
+        graph = graph_us_per_call(torch, qe, name, nbytes)
         out[str(rows)] = {"us_per_call": round(1e3 * iso, 3), "warm_us_per_call": round(1e3 * warm, 3),
-                          "host_us_per_call": round(1e3 * host, 3),
+                          "host_us_per_call": round(1e6 * host, 3),
+                          "graph_us_per_call": round(graph, 3),
+                          "graph_warm_us_per_call": round(graph_us_per_call(torch, qe, name, nbytes, True), 3),
                           "bytes": nbytes, "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
+                          "graph_gb_s": round(nbytes / (graph * 1e-6) / 1e9, 1),
                           "rotation_sets": t[name]["sets"]}
     return out
 
@@ -611,6 +647,8 @@ def main():
                          "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
                          "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                          "us_in_step": round(1e3 * marg, 3), "rotation_sets": t["sets"]}
+        if nbytes < 32 << 20:  # short launches: also without the Python launch cost
+            kernels[name]["graph_us_per_call"] = round(graph_us_per_call(torch, qe, name, nbytes), 3)
     extra = {} if args.only or args.no_extra else extra_timings(torch, qe, args.steps)
     norm_rows = {} if args.only or args.no_extra else norm_rows_timings(torch, qe, args.steps)
     split = {}
