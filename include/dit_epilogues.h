@@ -16,7 +16,13 @@
  *  - Static quantisation scales (`input_scale_dev`, `scale_dev`) are device
  *    pointers to ONE fp32 value, read by the kernel only. Preconditions that
  *    are documented but NOT checked: scales are finite and > 0, inputs are
- *    finite, and no output overlaps any input or another output.
+ *    finite, and no output overlaps any input or another output. Where a call
+ *    forms gate * x before a once-rounded sum (dit_bias_mul_add and the gated
+ *    residual of the dit_scale_residual_* calls), |gate * x| < 2^128 for
+ *    every element: the product is formed in fp32, which is exact below that
+ *    bound and overflows to +-inf above it. A product so small that fp32
+ *    holds only its sign (|gate * x| < 2^-149) can give +0 where the exact
+ *    sum is -0.
  *  - Return value: DIT_OK (0) or a dit_status code. On any refusal the call
  *    enqueues nothing and outputs are untouched, so a caller can fall back to
  *    an unfused path. The reason is also available from dit_last_error()
@@ -241,7 +247,8 @@ int dit_qkv_epilogue(void* joint_q, void* joint_k, void* joint_v,
  *   bias      [hidden] bf16, in, NULLABLE (no bias add)
  *   gate      [hidden] bf16, in
  *
- * hidden must be a multiple of 8 (and at most 2^30).
+ * hidden must be a multiple of 8 (and at most 2^30). |gate * (x + bias)| must
+ * stay below 2^128 (see the conventions above).
  */
 int dit_bias_mul_add(void* y, const void* x, const void* bias, const void* gate,
                      const void* residual, int64_t rows, int64_t hidden,

@@ -7,8 +7,9 @@
 // rounding; routing it through fp32 and then bf16 would round twice and break
 // product ties at large magnitudes.
 //
-// On gfx950 the product of two bf16 values is exact in fp32, so only the final
-// sum needs care: pack8_exact_sum rounds p + residual once.
+// On gfx950 the product of two bf16 values is exact in fp32 (below 2^128 in
+// magnitude, the library's input domain), so only the final sum needs care:
+// pack8_exact_sum rounds p + residual once.
 //
 // Layout: one workgroup of kThreads lanes per row; lane t takes the 16-byte
 // chunks t, t + kThreads, ... of the row (one chunk at hidden 3072), so each
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void bias_mul_add_kernel(BiasMulAddArgs a
         unpack8(rv, rf);
         float prod[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) prod[i] = xf[i] * gf[i];  // exact in fp32
+        for (int i = 0; i < 8; ++i) prod[i] = xf[i] * gf[i];  // exact in fp32 below 2^128
         uint32_t yw[4];
         pack8_exact_sum(prod, rf, yw);
         store16(yrow + 8 * c, (u32x4){yw[0], yw[1], yw[2], yw[3]});

@@ -74,7 +74,12 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
 }
 
 // bf16 of the EXACT sums p[i] + r[i] of fp32 values (one rounding each), two
-// per word, element 2j in the low half of word j. The fp32 sum s = RN32(p + r)
+// per word, element 2j in the low half of word j. The callers' p is a product
+// of two bf16 values, exact in fp32 (8 x 8 significant bits) for |p| below
+// 2^128, the bound of the library's input domain; a product too small for
+// fp32 keeps only its sign, which can turn a -0 result into +0. Checking for
+// both in the kernel measured 2-7% slower, so they stay outside the domain.
+// The fp32 sum s = RN32(p + r)
 // already rounds correctly to bf16 unless s lands exactly on a bf16 midpoint
 // (rounding is monotone and bf16 midpoints are fp32 values) AND the fp32 sum
 // was inexact; then the TwoSum error term says on which side the exact sum

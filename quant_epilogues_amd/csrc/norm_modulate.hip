@@ -167,8 +167,8 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
                 xf[i + 1] = bf_hi(w);
             }
         }
-        // gate * xb is exact in fp32 (8 x 8 significant bits); the sum with the
-        // residual is rounded once to bf16.
+        // gate * xb is exact in fp32 (8 x 8 significant bits, below 2^128 in
+        // magnitude); the sum with the residual is rounded once to bf16.
         float prod[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) prod[i] = gf[i] * xf[i];

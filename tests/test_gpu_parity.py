@@ -665,6 +665,67 @@ def test_hip_graph_capture_replays_match_eager(qe):
             assert torch.equal(v.view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
 
 
+def _bf16_band(rng, shape, exp_lo, exp_hi, sign=None):
+    """Random bf16 bit patterns with biased exponents in [exp_lo, exp_hi)."""
+    sign = rng.integers(0, 2, shape) if sign is None else sign
+    exp = rng.integers(exp_lo, exp_hi, shape)
+    man = rng.integers(0, 128, shape)
+    return ((sign << 15) | (exp << 7) | man).astype(np.uint16)
+
+
+@pytest.mark.parametrize("band", ["top", "bottom"])
+def test_fma_products_at_fp32_range_edges(qe, oracle_mod, e4m3_table, band):
+    """The single-rounded x * gate + residual at the edges of the products'
+    supported range (|x gate| < 2^128, where the fp32 product is exact):
+    products in [2^127, 1.72 * 2^127) against residuals of opposite sign near
+    the bf16 maximum (large cancellations, every result finite), and products
+    so small that fp32 underflows against zero or subnormal residuals. Both
+    bias_mul_add and the gated residual of the norm must reproduce the
+    oracle's exact rounding bit for bit; at the bottom only the sign of a zero
+    may differ (the library documents that a product fp32 cannot hold keeps
+    only its sign)."""
+    _print_case("fma at fp32 range edges", band)
+    rng = np.random.default_rng(11 if band == "top" else 12)
+    R, H = 4, 3072
+    if band == "top":
+        # unbiased factor exponents summing to 127, significands below 1.32
+        ge = rng.integers(188, 194, H)
+        gb = ((rng.integers(0, 2, H) << 15) | (ge << 7) | rng.integers(0, 41, H)).astype(np.uint16)
+        xs = rng.integers(0, 2, (R, H))
+        xb = ((xs << 15) | ((381 - ge)[None, :] << 7) | rng.integers(0, 41, (R, H))).astype(np.uint16)
+        prod_sign = (xs ^ (gb[None, :] >> 15)).astype(np.int64)
+        rb = (((1 - prod_sign) << 15) | (254 << 7) | rng.integers(0, 128, (R, H))).astype(np.uint16)
+    else:
+        xb = _bf16_band(rng, (R, H), 50, 66)
+        gb = _bf16_band(rng, (H,), 50, 66)
+        rb = _bf16_band(rng, (R, H), 0, 2)
+        rb[:, ::2] = 0  # half the residuals +0: the sum is the product alone
+    t = lambda b: dev(torch.from_numpy(b.view(np.int16)).view(torch.bfloat16))
+    u16 = lambda g: g.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    def same(name, gpu, ref):
+        if band == "bottom":  # +-0 compare equal
+            zero = ((gpu & 0x7FFF) == 0) & ((ref & 0x7FFF) == 0)
+            gpu, ref = np.where(zero, 0, gpu), np.where(zero, 0, ref)
+        check_exact(name, gpu, ref)
+
+    y = qe.bias_mul_add(t(xb), None, t(gb), t(rb))
+    same("bias_mul_add", u16(y), oracle_mod.bias_mul_add(xb, None, gb, rb))
+
+    scale = synth.bf16_bits((torch.randn(H, generator=torch.Generator().manual_seed(5)) * 0.1)
+                            .to(torch.bfloat16))
+    shift = synth.bf16_bits((torch.randn(H, generator=torch.Generator().manual_seed(6)) * 0.1)
+                            .to(torch.bfloat16))
+    r, yy, q = qe.scale_residual_norm_modulate_fp8(t(xb), None, t(gb), t(rb), t(scale), t(shift),
+                                                   dscalar(0.0625), 1e-6)
+    rr, ryy, rq, pre = oracle_mod.scale_residual_norm_modulate_fp8(
+        xb, None, gb, rb, scale, shift, float(np.float32(0.0625)), 1e-6)
+    assert np.isfinite(oracle_mod.f32_from_bf16(rr)).all()
+    same("residual_out", u16(r), rr)
+    check_bf16("y", u16(yy), ryy)
+    check_fp8("q", q.cpu().numpy(), rq, pre, e4m3_table)
+
+
 def test_degenerate_inputs(qe, oracle_mod, e4m3_table):
     """Constant, zero and outlier rows through the norms (with FP8 saturation
     and NVFP4), zero and huge heads through the QKV epilogue, and all-zero,
