@@ -129,30 +129,56 @@ __global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a, in
 // FP4 with the scales in 128x4 tiles. Inside a tile, the 32 rows m with the
 // same m % 32 / 8 hold one contiguous 128-byte line per tile column (4
 // groups): rows m0 + 32 i + r (i < 4, r < 8) for m0 = 128 t + 8 j. A
-// workgroup takes such a 32-row set and kTiledGroups groups: wave i computes
-// rows m0 + 32 i + r one after another (a lane per group, as in the
-// row-major kernel), stages the scale bytes in LDS, and after one barrier
-// the workgroup writes every line whole, 8 bytes per lane. Rows past `rows`
-// (up to the 128-row padding) only contribute zero scales. Needs groups % 4
-// == 0 (whole tile columns).
+// workgroup takes such a 32-row set and kTiledGroups groups: set row
+// s = 8 i + r is row m0 + 32 i + r, and each of the kTiledWaves waves takes
+// 32 / kTiledWaves consecutive set rows (a lane per group, as in the
+// row-major kernel), issuing all their loads before quantising any. The
+// scale bytes go to LDS, and after one barrier the first 256 lanes write
+// every line whole, 8 bytes per lane. Rows past `rows` (up to the 128-row
+// padding) only contribute zero scales. Needs groups % 4 == 0 (whole tile
+// columns). Eight waves of four rows measured 4% faster on MI355X than four
+// waves of eight rows taken one at a time.
 constexpr int kTiledGroups = 64;
+constexpr int kTiledWaves = 8;
+constexpr int kTiledRowsPerWave = 32 / kTiledWaves;
 
-__global__ __launch_bounds__(256) void token_cat_fp4_tiled_kernel(TokenCatArgs a) {
-    __shared__ uint8_t sbuf[32][kTiledGroups];  // [i * 8 + r][group in chunk]
+__global__ __launch_bounds__(64 * kTiledWaves) void token_cat_fp4_tiled_kernel(TokenCatArgs a) {
+    __shared__ uint8_t sbuf[32][kTiledGroups];  // [set row][group in chunk]
     const int lane = threadIdx.x & 63;
-    const int i = threadIdx.x >> 6;  // wave: rows m0 + 32 i + r
+    const int wave = threadIdx.x >> 6;
     const int64_t cols = a.a_cols + a.b_cols;
     const int groups = (int)(cols >> 4);
     const int g0 = blockIdx.x * kTiledGroups;
     const int64_t m0 = (int64_t)(blockIdx.y >> 2) * 128 + (blockIdx.y & 3) * 8;
     const float gscale = *a.scale;  // global inverse scale
     const int g = g0 + lane;
-    for (int r = 0; r < 8; ++r) {
-        const int64_t row = m0 + 32 * i + r;
+    u32x4 raw[kTiledRowsPerWave][2];
+    bool ok[kTiledRowsPerWave];
+#pragma unroll
+    for (int t = 0; t < kTiledRowsPerWave; ++t) {
+        const int sr = wave * kTiledRowsPerWave + t;
+        const int64_t row = m0 + 32 * (sr >> 3) + (sr & 7);
+        ok[t] = row < a.rows && g < groups;
+        if (ok[t]) {
+            const uint16_t* src = cat_source(a, row, g);
+            raw[t][0] = stream_load16(src);
+            raw[t][1] = stream_load16(src + 8);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kTiledRowsPerWave; ++t) {
+        const int sr = wave * kTiledRowsPerWave + t;
+        const int64_t row = m0 + 32 * (sr >> 3) + (sr & 7);
         uint32_t s8 = 0;
-        if (row < a.rows && g < groups) {
-            float f[16];
-            load16x2(cat_source(a, row, g), f);
+        if (ok[t]) {
+            float lo[8], hi[8], f[16];
+            unpack8(raw[t][0], lo);
+            unpack8(raw[t][1], hi);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f[e] = lo[e];
+                f[8 + e] = hi[e];
+            }
             float amax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[e]));
@@ -172,12 +198,14 @@ __global__ __launch_bounds__(256) void token_cat_fp4_tiled_kernel(TokenCatArgs a
             }
             store8(a.out + row * (cols >> 1) + 8 * g, packed);
         }
-        sbuf[i * 8 + r][lane] = (uint8_t)s8;
+        sbuf[sr][lane] = (uint8_t)s8;
     }
     __syncthreads();
-    // Lines: kTiledGroups / 4 tile columns x 128 bytes; lane t writes bytes
-    // 8 (t % 16) .. +7 of line t / 16. Byte p of a line is row m0 + 32 ((p % 16)
-    // / 4) + p / 16, group 4 * column + p % 4.
+    // Lines: kTiledGroups / 4 tile columns x 128 bytes; lane t < 256 writes
+    // bytes 8 (t % 16) .. +7 of line t / 16. Byte p of a line is row
+    // m0 + 32 ((p % 16) / 4) + p / 16 (set row 8 ((p % 16) / 4) + p / 16),
+    // group 4 * column + p % 4.
+    if (threadIdx.x >= 16 * (kTiledGroups / 4)) return;
     const int col = threadIdx.x >> 4;
     const int gc = g0 + 4 * col;
     if (gc >= groups) return;
@@ -238,7 +266,7 @@ hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream) {
             b.out_scales = a.out_scales + set0 * 32 * groups;
             b.rows = a.rows - set0 * 32;
             hipLaunchKernelGGL(token_cat_fp4_tiled_kernel, dim3((unsigned)chunks, (unsigned)n),
-                               dim3(256), 0, stream, b);
+                               dim3(64 * kTiledWaves), 0, stream, b);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
