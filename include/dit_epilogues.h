@@ -107,7 +107,8 @@ int dit_norm_modulate_fp8(void* y, uint8_t* q, const void* x, const void* scale,
  *
  *   residual_out [rows, hidden] bf16, out:
  *       bf16(residual + gate * xb) with ONE rounding, xb = bf16(x + bias)
- *       (xb = x when bias is NULL)
+ *       (xb = x when bias is NULL); |gate * xb| below 2^128 (see the
+ *       conventions above)
  *   y, q         as dit_norm_modulate_fp8 (either may be NULL), computed
  *                from residual_out; q == NULL is the bf16-only bias + gated
  *                residual norm of the sglang PR 37116 page
