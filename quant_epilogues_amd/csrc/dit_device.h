@@ -137,6 +137,17 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)w;
 }
 
+// a / 6 (IEEE fp32, round to nearest even) for a non-negative bf16 value a
+// held in fp32: the product with RN(1/6) and one FMA correction step. Checked
+// equal to the IEEE quotient for every non-negative finite bf16 value (with
+// fp32 denormals preserved, as these kernels run); +inf passes through.
+__device__ __forceinline__ float div6_bf16(float a) {
+    const float c = 0x1.555556p-3f;  // RN(1/6)
+    const float q0 = a * c;
+    const float q = __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), c, q0);
+    return a == __builtin_inff() ? a : q;
+}
+
 // Value of a non-negative E4M3FN code (sign bit clear, not NaN).
 __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
     const uint32_t e = c >> 3, m = c & 7u;

@@ -123,8 +123,15 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
 
     // 2. Column vectors to fp32 in LDS, while the streaming loads are in
     // flight; one vector at a time, which keeps the kernel's register peak
-    // (and so its occupancy) where the streaming loads alone put it.
+    // (and so its occupancy) where the streaming loads alone put it. With FP4
+    // output the table g / value(code) of the 126 nonzero E4M3 scale codes
+    // follows them (the same IEEE divisions, done once per workgroup).
+    float* kq_tab = cols + (size_t)kColVecs<MODE> * H;
     if (kLds) {
+        if constexpr (kFp4) {
+            for (int code = threadIdx.x; code < 128; code += blockDim.x)
+                kq_tab[code] = (code != 0 && code < 127) ? g4 / e4m3_value_pos(code) : 0.0f;
+        }
         for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
 #pragma unroll 1
             for (int which = 0; which < kColVecs<MODE>; ++which) {
@@ -272,12 +279,12 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
             const float other = __builtin_bit_cast(
                 float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false));
             amax = __builtin_fmaxf(amax, other);  // quad_perm [1, 0, 3, 2]
-            const float s_pre = (amax / 6.0f) * g4;
+            const float s_pre = div6_bf16(amax) * g4;  // amax is a bf16 value
             const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
                                     __builtin_fminf(s_pre, 448.0f), 0.0f, 0, false) & 0xFFu;
             uint32_t packed = 0;
             if (s8 != 0) {
-                const float kq = g4 / e4m3_value_pos(s8);  // IEEE division
+                const float kq = kLds ? kq_tab[s8] : g4 / e4m3_value_pos(s8);  // IEEE division
                 float t[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) t[i] = yv[i] * kq;
@@ -319,7 +326,7 @@ hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
     const int64_t grid_rows = kFp4 ? a.fp4_rows_padded : a.rows;
     const uint64_t blocks = (uint64_t)((grid_rows + RPW - 1) / RPW);
     if (blocks * (64 * WPR * RPW) >= kMaxGridLanes) return kGridTooLarge;
-    const size_t lds = kLds ? (size_t)kColVecs<MODE> * a.hidden * sizeof(float) : 0;
+    const size_t lds = kLds ? ((size_t)kColVecs<MODE> * a.hidden + (kFp4 ? 128 : 0)) * sizeof(float) : 0;
     const dim3 grid((unsigned)blocks), block(64 * WPR * RPW);
     if (MODE == kPlain && a.hidden == 512 * WPR * V)
         hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4, true, kHoist>), grid,

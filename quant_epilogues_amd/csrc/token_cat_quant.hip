@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a, in
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[e]));
-    const float s_pre = (amax / 6.0f) * gscale;
+    const float s_pre = div6_bf16(amax) * gscale;  // amax is a bf16 value
     const uint32_t s8 =
         (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s_pre, 448.0f), 0.0f, 0, false) & 0xFFu;
     u32x2 packed = {0u, 0u};
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64 * kTiledWaves) void token_cat_fp4_tiled_kernel(T
             float amax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[e]));
-            const float s_pre = (amax / 6.0f) * gscale;
+            const float s_pre = div6_bf16(amax) * gscale;  // amax is a bf16 value
             s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s_pre, 448.0f), 0.0f, 0,
                                                            false) & 0xFFu;
             u32x2 packed = {0u, 0u};

@@ -726,6 +726,30 @@ def test_fma_products_at_fp32_range_edges(qe, oracle_mod, e4m3_table, band):
     check_fp8("q", q.cpu().numpy(), rq, pre, e4m3_table)
 
 
+@pytest.mark.parametrize("g", [1.0, 2.0 ** -60, 2.0 ** -120, 2.0 ** 60])
+def test_fp4_group_scale_for_every_bf16_maximum(qe, oracle_mod, e4m3_table, g):
+    """Every finite non-negative bf16 value as a 16-element group's maximum
+    (one group per value, the rest of the group zero; signs alternate), under
+    global scales that bring small and huge maxima into the unclamped range of
+    the E4M3 group scale: the scale bytes, which depend on amax / 6 rounded
+    once, must equal the oracle's exactly, and the codes within the FP4 rule."""
+    _print_case("fp4 group scale, every bf16 maximum", g)
+    n = 0x7F80  # +0 .. the largest finite bf16
+    cols = 256  # 16 groups per row
+    rows = -(-n // (cols // 16))
+    x = np.zeros((rows, cols), np.uint16)
+    amax = np.arange(rows * (cols // 16), dtype=np.int64) % n
+    sign = (np.arange(rows * (cols // 16)) % 2).astype(np.uint16) << 15
+    x.reshape(-1, 16)[:, 0] = amax.astype(np.uint16) | sign
+    x.reshape(-1, 16)[:, 7] = (amax // 2).astype(np.uint16)  # a smaller second value
+    t = dev(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+    packed, scales = qe.token_cat_quant(qe.DIT_QUANT_FP4_E2M1, t, None, dscalar(g))
+    rp, rs, s_pre, pre = oracle_mod.token_cat_fp4(x, np.zeros((rows, 0), np.uint16), g)
+    check_exact("scales", scales.cpu().numpy(), rs)
+    check_fp4("fp4", packed.cpu().numpy(), scales.cpu().numpy(), rp, rs, s_pre, pre,
+              oracle_mod.f32_from_bf16(x), g, e4m3_table, oracle_mod.e2m1_encode)
+
+
 def test_degenerate_inputs(qe, oracle_mod, e4m3_table):
     """Constant, zero and outlier rows through the norms (with FP8 saturation
     and NVFP4), zero and huge heads through the QKV epilogue, and all-zero,
