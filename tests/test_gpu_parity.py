@@ -254,6 +254,36 @@ def test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, resid, with_bias, wa
     print("exact: " + " ".join(msg))
 
 
+# Widths whose chunks per row (66, 130, 260, 384, 450, 700, 800) land in every
+# case of the norm launcher's width switches: one, two and three chunks per
+# lane at two waves per row (384: the exact fit), the six-wave plain geometry,
+# eight chunks per lane, one-wave residual rows with 2..6 chunks per lane and
+# the two-wave residual geometry with 4, 6 and 8; at 37 rows the latency path
+# with one, two and three chunks per lane.
+GEOMETRY_WIDTHS = [528, 1040, 2080, 3072, 3600, 5600, 6400]
+
+
+@pytest.mark.parametrize("rows", [1031, 37])
+@pytest.mark.parametrize("hidden", GEOMETRY_WIDTHS)
+def test_norm_every_geometry(qe, oracle_mod, e4m3_table, rows, hidden):
+    """Every kernel instance the norm launcher can pick for these widths, at a
+    row count on the many-rows path (1031: a partial last workgroup) and one
+    on the latency path (37): the plain norm and both residual variants with
+    both outputs, and NVFP4 output with and without the residual (128x4
+    scales where the width allows)."""
+    seed = 7 * hidden + rows
+    test_norm_output_selection(qe, oracle_mod, e4m3_table, rows, hidden, 0.0625,
+                               False, False, True, True, seed)
+    test_norm_output_selection(qe, oracle_mod, e4m3_table, rows, hidden, 0.0625,
+                               True, True, True, True, seed + 1)
+    test_norm_output_selection(qe, oracle_mod, e4m3_table, rows, hidden, 0.0625,
+                               True, False, True, True, seed + 2)
+    test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, True, True, True, 448.0, False,
+                  seed + 3)
+    test_norm_fp4(qe, oracle_mod, e4m3_table, rows, hidden, False, False, True, 448.0,
+                  hidden % 64 == 0, seed + 4)
+
+
 def test_fp8_split_equals_fused_on_gpu(qe):
     """q of the fused kernel == y re-quantised by the token-cat FP8 path."""
     inp = synth.norm_modulate_inputs(256, 3072, seed=21, input_scale=0.4754464328)
