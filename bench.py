@@ -611,7 +611,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: these epilogues need no cross-GPU exchange and "
-              "this build runs on a single MI355X; run with --gpus 1", file=sys.stderr)
+              "each launch runs on one MI355X; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
