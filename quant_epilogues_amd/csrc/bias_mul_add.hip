@@ -11,27 +11,31 @@
 // magnitude, the library's input domain), so only the final sum needs care:
 // pack8_exact_sum rounds p + residual once.
 //
-// Layout: one workgroup of kThreads lanes per row; lane t takes the 16-byte
-// chunks t, t + kThreads, ... of the row (one chunk at hidden 3072), so each
+// Layout: one wave64 per workgroup, one 64-chunk segment of a row per wave;
+// lane t of segment s takes the 16-byte chunk 64 s + t of its row, so each
 // instruction of a wave moves 1 KiB of contiguous HBM and consecutive
-// workgroups sweep memory in address order. x and residual stream through
-// with non-temporal loads; bias and gate are row-broadcast and stay in L2.
+// workgroups (segments of a row, then the next row) sweep memory in address
+// order. One-wave workgroups are dispatched and retired independently; on
+// MI355X they streamed this shape 6% faster than one six-wave workgroup per
+// row. x and residual stream through with non-temporal loads; bias and gate
+// are row-broadcast and stay in L2.
 #include "dit_device.h"
 #include "kernels.h"
 
 namespace dit {
 namespace {
 
-constexpr int kThreads = 384;  // six waves: 3072 columns in one pass
+constexpr int kThreads = 64;  // one wave, one 64-chunk (512-column) segment of a row
 
 template <bool kHasBias>
-__global__ __launch_bounds__(kThreads) void bias_mul_add_kernel(BiasMulAddArgs a) {
-    const int64_t row = blockIdx.x;
+__global__ __launch_bounds__(kThreads) void bias_mul_add_kernel(BiasMulAddArgs a, int segs) {
+    const int64_t row = blockIdx.x / (unsigned)segs;
+    const int c = (int)(blockIdx.x % (unsigned)segs) * kThreads + (int)threadIdx.x;
     const int cpr = (int)(a.hidden >> 3);
     const uint16_t* xrow = a.x + row * a.hidden;
     const uint16_t* rrow = a.residual + row * a.hidden;
     uint16_t* yrow = a.y + row * a.hidden;
-    for (int c = threadIdx.x; c < cpr; c += kThreads) {
+    if (c < cpr) {
         const u32x4 xv = stream_load16(xrow + 8 * c);
         const u32x4 rv = stream_load16(rrow + 8 * c);
         float xf[8], rf[8], gf[8];
@@ -61,10 +65,11 @@ __global__ __launch_bounds__(kThreads) void bias_mul_add_kernel(BiasMulAddArgs a
 
 template <bool kHasBias>
 hipError_t launch_bias(const BiasMulAddArgs& a, hipStream_t stream) {
-    const uint64_t blocks = (uint64_t)a.rows;
+    const int segs = (int)(((a.hidden >> 3) + kThreads - 1) / kThreads);  // segments per row
+    const uint64_t blocks = (uint64_t)a.rows * (uint64_t)segs;
     if (blocks * kThreads >= kMaxGridLanes) return kGridTooLarge;
     hipLaunchKernelGGL(bias_mul_add_kernel<kHasBias>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, a);
+                       stream, a, segs);
     return hipGetLastError();
 }
 

@@ -15,8 +15,8 @@
 // k = g / value(s8), code = e2m1(x * k); a zero scale gives zero codes.
 //
 // Layout on gfx950: one workgroup per (row, tile of chunks), numbered in
-// address order. FP8: each lane takes
-// 8-element chunks (one 16-byte streaming load -> one 8-byte store), so every
+// address order. FP8: a workgroup is one wave and each lane takes one
+// 8-element chunk (one 16-byte streaming load -> one 8-byte store), so every
 // load instruction of a wave reads 1 KiB contiguously. FP4: one lane per
 // 16-element group (two 16-byte loads -> 8 packed bytes + 1 scale byte; a
 // wave's 64 scale bytes are contiguous). Chunks and groups never straddle the
@@ -27,7 +27,12 @@
 namespace dit {
 namespace {
 
-constexpr int kTile = 256;  // chunks (or groups) per workgroup
+// Lanes per workgroup. FP8: one wave; on MI355X one-wave workgroups streamed
+// the FLUX.2 shape 6% faster than four-wave ones (they are dispatched and
+// retired independently). FP4: four waves, which measured 2% faster there
+// than one.
+constexpr int kFp8Tile = 64;
+constexpr int kTile = 256;
 
 __device__ __forceinline__ const uint16_t* cat_source(const TokenCatArgs& a, int64_t row, int c16) {
     const int a_chunks = (int)(a.a_cols >> 4);
@@ -54,11 +59,12 @@ __device__ __forceinline__ void row_tile(int64_t row0, int64_t& row, int& tile) 
     tile = (int)blockIdx.x;
 }
 
-// FP8: U chunks of 8 elements per thread, kTile apart, so a workgroup covers
-// U * kTile chunks and each load instruction of a wave reads 1 KiB of one row
-// contiguously (one 16-byte streaming load -> one 8-byte store per chunk).
+// FP8: U chunks of 8 elements per thread, kFp8Tile apart, so a workgroup
+// covers U * kFp8Tile chunks and each load instruction of a wave reads 1 KiB
+// of one row contiguously (one 16-byte streaming load -> one 8-byte store per
+// chunk).
 template <int U>
-__global__ __launch_bounds__(kTile) void token_cat_fp8_kernel(TokenCatArgs a, int64_t row0) {
+__global__ __launch_bounds__(kFp8Tile) void token_cat_fp8_kernel(TokenCatArgs a, int64_t row0) {
     int64_t row;
     int tile;
     row_tile(row0, row, tile);
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kTile) void token_cat_fp8_kernel(TokenCatArgs a, in
     float f[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int c = (tile * U + u) * kTile + threadIdx.x;
+        const int c = (tile * U + u) * kFp8Tile + threadIdx.x;
         if (c >= cpr) continue;
         const uint16_t* src = c < a_chunks ? a.a + row * a.a_cols + 8 * c
                                            : a.b + row * a.b_cols + 8 * (c - a_chunks);
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(kTile) void token_cat_fp8_kernel(TokenCatArgs a, in
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int c = (tile * U + u) * kTile + threadIdx.x;
+        const int c = (tile * U + u) * kFp8Tile + threadIdx.x;
         if (c >= cpr) continue;
         const uint32_t w0 = pack_e4m3x4(clamp_e4m3(f[u][0] * inv), clamp_e4m3(f[u][1] * inv),
                                         clamp_e4m3(f[u][2] * inv), clamp_e4m3(f[u][3] * inv));
@@ -226,28 +232,30 @@ __global__ __launch_bounds__(64 * kTiledWaves) void token_cat_fp4_tiled_kernel(T
 constexpr int64_t kRowsPerLaunch = 65536;
 
 template <typename Kernel>
-hipError_t launch_rows_tiles(Kernel kernel, const TokenCatArgs& a, int64_t rows, int64_t per_tile,
-                             int64_t units_per_row, hipStream_t stream) {
+hipError_t launch_rows_tiles(Kernel kernel, int threads, const TokenCatArgs& a, int64_t rows,
+                             int64_t per_tile, int64_t units_per_row, hipStream_t stream) {
     const int64_t tiles = (units_per_row + per_tile - 1) / per_tile;
-    if ((uint64_t)tiles * kTile >= kMaxGridLanes) return kGridTooLarge;
+    if ((uint64_t)tiles * threads >= kMaxGridLanes) return kGridTooLarge;
     for (int64_t row0 = 0; row0 < rows; row0 += kRowsPerLaunch) {
         const int64_t n = rows - row0 < kRowsPerLaunch ? rows - row0 : kRowsPerLaunch;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)tiles, (unsigned)n), dim3(kTile), 0, stream, a, row0);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)tiles, (unsigned)n), dim3(threads), 0, stream, a,
+                           row0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-constexpr int kFp8ChunksPerThread = 2;
+constexpr int kFp8ChunksPerThread = 1;
 
 }  // namespace
 
-// Two 8-element chunks per thread measured best on MI355X at
-// 4608 x (6144 + 18432).
+// One 8-element chunk per thread in one-wave workgroups measured best on
+// MI355X at 4608 x (6144 + 18432) (two chunks: 1% slower).
 hipError_t launch_token_cat_fp8(const TokenCatArgs& a, hipStream_t stream) {
-    return launch_rows_tiles(token_cat_fp8_kernel<kFp8ChunksPerThread>, a, a.rows,
-                             (int64_t)kFp8ChunksPerThread * kTile, (a.a_cols + a.b_cols) / 8, stream);
+    return launch_rows_tiles(token_cat_fp8_kernel<kFp8ChunksPerThread>, kFp8Tile, a, a.rows,
+                             (int64_t)kFp8ChunksPerThread * kFp8Tile, (a.a_cols + a.b_cols) / 8,
+                             stream);
 }
 
 // One lane per 16-element group measured faster than two lanes per group.
@@ -272,8 +280,8 @@ hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream) {
         }
         return hipSuccess;
     }
-    return launch_rows_tiles(token_cat_fp4_kernel, a, rows_padded, kTile, (a.a_cols + a.b_cols) / 16,
-                             stream);
+    return launch_rows_tiles(token_cat_fp4_kernel, kTile, a, rows_padded, kTile,
+                             (a.a_cols + a.b_cols) / 16, stream);
 }
 
 }  // namespace dit
