@@ -36,13 +36,19 @@ __global__ __launch_bounds__(kThreads) void bias_mul_add_kernel(BiasMulAddArgs a
     const uint16_t* rrow = a.residual + row * a.hidden;
     uint16_t* yrow = a.y + row * a.hidden;
     if (c < cpr) {
+        // All four loads are issued before any of them is used: the
+        // scheduling barrier keeps the compiler from waiting on the gate's
+        // L2 round trip before it issues the bias load.
         const u32x4 xv = stream_load16(xrow + 8 * c);
         const u32x4 rv = stream_load16(rrow + 8 * c);
+        const u32x4 gv = load16(a.gate + 8 * c);
+        const u32x4 bv = kHasBias ? load16(a.bias + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
+        __builtin_amdgcn_sched_barrier(0);
         float xf[8], rf[8], gf[8];
-        unpack8(load16(a.gate + 8 * c), gf);
+        unpack8(gv, gf);
         if (kHasBias) {
             float bf[8];
-            unpack8(load16(a.bias + 8 * c), bf);
+            unpack8(bv, bf);
             unpack8(xv, xf);
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {  // b = bf16(x + bias)

@@ -57,7 +57,7 @@ struct QkvArgs {
 };
 constexpr int kHeadDim = 128;
 constexpr int kMaxHeads = 64;
-constexpr int kQkvHeadsPerWave = 24;  // heads handled by one wave of the QKV kernel
+constexpr int kQkvHeadsPerWave = 12;  // heads handled by one wave of the QKV kernel
 hipError_t launch_qkv_epilogue(const QkvArgs& a, hipStream_t stream);
 
 struct BiasMulAddArgs {

@@ -17,38 +17,27 @@
 // Layout on gfx950: one workgroup per (row, tile of chunks), numbered in
 // address order. FP8: a workgroup is one wave and each lane takes one
 // 8-element chunk (one 16-byte streaming load -> one 8-byte store), so every
-// load instruction of a wave reads 1 KiB contiguously. FP4: one lane per
-// 16-element group (two 16-byte loads -> 8 packed bytes + 1 scale byte; a
-// wave's 64 scale bytes are contiguous). Chunks and groups never straddle the
-// branch boundary because both widths are multiples of 16.
+// load instruction of a wave reads 1 KiB contiguously. FP4: a workgroup is
+// one wave and each lane takes one 16-byte half of a 16-element group per
+// load (the two halves of a group sit in adjacent lanes and exchange their
+// maxima), so FP4 loads are contiguous 1 KiB per instruction too. Chunks and
+// groups never straddle the branch boundary because both widths are
+// multiples of 16.
 #include "dit_device.h"
 #include "kernels.h"
 
 namespace dit {
 namespace {
 
-// Lanes per workgroup. FP8: one wave; on MI355X one-wave workgroups streamed
-// the FLUX.2 shape 6% faster than four-wave ones (they are dispatched and
-// retired independently). FP4: four waves, which measured 2% faster there
-// than one.
+// Lanes per workgroup: one wave. On MI355X one-wave workgroups streamed the
+// FLUX.2 shape 6% faster than four-wave ones (they are dispatched and retired
+// independently).
 constexpr int kFp8Tile = 64;
-constexpr int kTile = 256;
 
 __device__ __forceinline__ const uint16_t* cat_source(const TokenCatArgs& a, int64_t row, int c16) {
     const int a_chunks = (int)(a.a_cols >> 4);
     return c16 < a_chunks ? a.a + row * a.a_cols + 16 * c16
                           : a.b + row * a.b_cols + 16 * (c16 - a_chunks);
-}
-
-__device__ __forceinline__ void load16x2(const uint16_t* src, float (&f)[16]) {
-    float lo[8], hi[8];
-    unpack8(stream_load16(src), lo);
-    unpack8(stream_load16(src + 8), hi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        f[e] = lo[e];
-        f[8 + e] = hi[e];
-    }
 }
 
 // The grid is (tile, row - row0): the tile index varies fastest, so consecutive
@@ -93,43 +82,63 @@ __global__ __launch_bounds__(kFp8Tile) void token_cat_fp8_kernel(TokenCatArgs a,
     }
 }
 
-// FP4: one lane per 16-element group (two 16-byte loads -> 8 packed bytes and
-// one scale byte); rows past `rows` only write their zero scales.
-__global__ __launch_bounds__(kTile) void token_cat_fp4_kernel(TokenCatArgs a, int64_t row0) {
+// FP4, row-major scales: one wave per (row, 32 * kFp4Loads groups). Load t
+// of lane l reads half-group piece 64 t + l of the wave's span (a 16-byte
+// streaming load, element pieces in address order); the two halves of a
+// group sit in adjacent lanes and exchange their maxima by DPP, so each lane
+// quantises its 8 values (4 packed bytes) with the group's scale and even
+// lanes write the scale byte. Rows past `rows` (up to the 128-row padding)
+// only write zero scales. Two loads per lane measured best on MI355X at
+// 4608 x 24576: 7% faster than one lane per whole group in four-wave
+// workgroups, and than one or four loads per lane.
+constexpr int kFp4Loads = 2;
+
+__global__ __launch_bounds__(64) void token_cat_fp4_kernel(TokenCatArgs a, int64_t row0) {
     int64_t row;  // < round_up(rows, 128)
     int tile;
     row_tile(row0, row, tile);
+    const int lane = threadIdx.x;
     const int64_t cols = a.a_cols + a.b_cols;
     const int groups = (int)(cols >> 4);
-    const int g = tile * kTile + threadIdx.x;
-    if (g >= groups) return;
-    uint8_t* scale_out = a.out_scales + fp4_scale_offset(row, g, groups, a.scales_tiled);
-    if (row >= a.rows) {  // pad rows of the scale matrix
-        *scale_out = 0;
-        return;
+    const int p0 = tile * (64 * kFp4Loads);  // first half-group piece of the wave
+    const float gscale = *a.scale;           // global inverse scale
+    const bool live = row < a.rows;          // wave-uniform
+    u32x4 raw[kFp4Loads];
+#pragma unroll
+    for (int t = 0; t < kFp4Loads; ++t) {
+        const int pc = p0 + 64 * t + lane;
+        const int g = pc >> 1;
+        raw[t] = (live && g < groups) ? stream_load16(cat_source(a, row, g) + 8 * (pc & 1))
+                                      : (u32x4){0, 0, 0, 0};
     }
-    const float gscale = *a.scale;  // global inverse scale
-    float f[16];
-    load16x2(cat_source(a, row, g), f);
-    float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[e]));
-    const float s_pre = div6_bf16(amax) * gscale;  // amax is a bf16 value
-    const uint32_t s8 =
-        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s_pre, 448.0f), 0.0f, 0, false) & 0xFFu;
-    u32x2 packed = {0u, 0u};
-    if (s8 != 0) {
-        const float kq = gscale / e4m3_value_pos(s8);  // IEEE division
-        float t0[8], t1[8];
+    for (int t = 0; t < kFp4Loads; ++t) {
+        const int pc = p0 + 64 * t + lane;
+        const int g = pc >> 1;
+        float f[8];
+        unpack8(raw[t], f);
+        float amax = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            t0[e] = f[e] * kq;
-            t1[e] = f[8 + e] * kq;
+        for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[e]));
+        const float other = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false));
+        amax = __builtin_fmaxf(amax, other);  // quad_perm [1, 0, 3, 2]: the group's other half
+        const float s_pre = div6_bf16(amax) * gscale;  // amax is a bf16 value
+        const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(s_pre, 448.0f),
+                                                                      0.0f, 0, false) & 0xFFu;
+        uint32_t w = 0;
+        if (s8 != 0) {
+            const float kq = gscale / e4m3_value_pos(s8);  // IEEE division
+            float q[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = f[e] * kq;
+            w = pack_e2m1x8(q);
         }
-        packed = (u32x2){pack_e2m1x8(t0), pack_e2m1x8(t1)};
+        if (g < groups) {
+            if (live) store4(a.out + row * (cols >> 1) + 4 * pc, w);
+            if ((lane & 1) == 0) a.out_scales[row * groups + g] = (uint8_t)s8;
+        }
     }
-    store8(a.out + row * (cols >> 1) + 8 * g, packed);
-    *scale_out = (uint8_t)s8;
 }
 
 // FP4 with the scales in 128x4 tiles. Inside a tile, the 32 rows m with the
@@ -249,7 +258,6 @@ hipError_t launch_token_cat_fp8(const TokenCatArgs& a, hipStream_t stream) {
                              stream);
 }
 
-// One lane per 16-element group measured faster than two lanes per group.
 hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream) {
     const int64_t rows_padded = (a.rows + 127) / 128 * 128;
     if (a.scales_tiled) {
@@ -271,7 +279,7 @@ hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream) {
         }
         return hipSuccess;
     }
-    return launch_rows_tiles(token_cat_fp4_kernel, kTile, a, rows_padded, kTile,
+    return launch_rows_tiles(token_cat_fp4_kernel, 64, a, rows_padded, 32 * kFp4Loads,
                              (a.a_cols + a.b_cols) / 16, stream);
 }
 
