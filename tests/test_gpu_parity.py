@@ -302,10 +302,12 @@ QKV_CASES = [
     (4096, 512, 24, 0, False),   # Qwen-Image 1024^2: 4096 image + 512 text tokens
     (5, 3, 3, 1, False),         # heads not a multiple of 4
     (7, 2, 24, 2, False),
-    (3, 4, 48, 3, True),         # FLUX.2 head count (two 24-head waves), shared cache
+    (3, 4, 48, 3, True),         # FLUX.2 head count (four 12-head waves), shared cache
     (2, 1, 64, 4, False),
     (6, 0, 24, 5, True),         # image only
     (0, 5, 5, 6, True),          # text only
+    (3, 2, 30, 7, False),        # three head groups, the last one partial
+    (2, 3, 60, 8, True),         # five head groups
 ]
 
 
@@ -530,7 +532,16 @@ def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed
     print(f"exact: codes {ec:.6f} scales {es:.6f}")
 
 
-@pytest.mark.parametrize("rows,a_cols,b_cols,seed", [(4608, 6144, 18432, 50), (130, 64, 192, 51)])
+FP4_128X4_CASES = [
+    (4608, 6144, 18432, 50),  # FLUX.2 single block
+    (130, 64, 192, 51),       # 16 groups: one wave's four tile columns; two row tiles
+    (33, 64, 128, 52),        # 12 groups: a wave with three of its four tile columns
+    (300, 1024, 1088, 53),    # 132 groups: the last wave holds one tile column; three row tiles
+    (129, 6144, 64, 54),      # 388 groups, the branch boundary inside a wave's span
+]
+
+
+@pytest.mark.parametrize("rows,a_cols,b_cols,seed", FP4_128X4_CASES)
 def test_token_cat_fp4_128x4_scales(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, seed):
     """FP4 token concatenation with the scales in the 128x4 tile layout: the
     packed codes equal the row-major run's and the scale bytes equal the
