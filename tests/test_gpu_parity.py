@@ -152,6 +152,8 @@ SELECT_CASES = [
     (127, 3072, 0.0625, False, False, True, False, 33),
     (17, 1000, 0.5, True, False, False, True, 34),
     (1030, 4104, 0.0625, False, False, False, True, 35),  # FP8 only, 513 chunks per row
+    (1031, 6144, 0.5, False, False, False, True, 36),     # scale/shift parked in LDS; the last
+                                                          # workgroup's second row slot is empty
 ]
 
 
