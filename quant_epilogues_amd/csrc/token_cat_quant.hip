@@ -144,28 +144,31 @@ __global__ __launch_bounds__(64) void token_cat_fp4_kernel(TokenCatArgs a, int64
 // FP4 with the scales in 128x4 tiles. Inside a tile, the 32 rows m with the
 // same m % 32 / 8 hold one contiguous 128-byte line per tile column (4
 // groups): rows m0 + 32 i + r (i < 4, r < 8) for m0 = 128 t + 8 j, and dword
-// 4 r + i of the line holds the scales of row m0 + 32 i + r. A workgroup is
-// one wave and takes such a 32-row set over kTiledCols tile columns
-// (kTiledGroups groups, 512 bytes of each row). Set row s = 8 i + r is row
-// m0 + 32 i + r. Each lane loads one 16-byte half group per row: a load
+// 4 r + i of the line holds the scales of row m0 + 32 i + r. A workgroup
+// takes such a 32-row set over kTiledCols tile columns (kTiledGroups groups,
+// 512 bytes of each row) with kTiledSetWaves waves. Set row s = 8 i + r is
+// row m0 + 32 i + r. Each lane loads one 16-byte half group per row: a load
 // instruction covers kTiledRowsPerLoad rows, 512 contiguous bytes each, and
-// the wave issues all 32 rows' loads before quantising any. The two halves
-// of a group sit in adjacent lanes and exchange their maxima by DPP. The
-// scale bytes go to LDS, and the wave then writes every line whole, one
-// dword per lane. Rows past `rows` (up to the 128-row padding) only
-// contribute zero scales. Needs groups % 4 == 0 (whole tile columns). On
-// MI355X this measured 6% faster than eight waves of four rows sharing the
-// lines through LDS, and two or eight tile columns per wave were slower.
+// each wave issues its kTiledLoads loads (its four set rows) before
+// quantising any. The two halves of a group sit in adjacent lanes and
+// exchange their maxima by DPP. The scale bytes go to LDS, and after one
+// barrier the first 128 lanes write every line whole, one dword per lane.
+// Rows past `rows` (up to the 128-row padding) only contribute zero scales.
+// Needs groups % 4 == 0 (whole tile columns). Measured on MI355X at
+// 4608 x 24576 with 1, 2, 4, 8 and 16 waves per set: 50.5, 48.5, 46.7, 44.8
+// and 62.8 us; eight tile columns with eight waves: 47.6 us.
 constexpr int kTiledCols = 4;
-constexpr int kTiledGroups = 4 * kTiledCols;                 // groups per wave
+constexpr int kTiledGroups = 4 * kTiledCols;                 // groups per workgroup
 constexpr int kTiledLanesPerRow = 2 * kTiledGroups;         // one 16-byte half group per lane
 constexpr int kTiledRowsPerLoad = 64 / kTiledLanesPerRow;   // rows per load instruction
-constexpr int kTiledLoads = 32 / kTiledRowsPerLoad;         // load instructions for 32 rows
+constexpr int kTiledSetWaves = 8;                           // waves sharing a 32-row set
+constexpr int kTiledLoads = 32 / kTiledRowsPerLoad / kTiledSetWaves;  // load instructions per wave
 
-__global__ __launch_bounds__(64) void token_cat_fp4_tiled_kernel(TokenCatArgs a) {
+__global__ __launch_bounds__(64 * kTiledSetWaves) void token_cat_fp4_tiled_kernel(TokenCatArgs a) {
     __shared__ uint32_t sbuf32[32 * kTiledGroups / 4];  // [set row][group] scale bytes
     uint8_t* sbuf = reinterpret_cast<uint8_t*>(sbuf32);
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;  // this wave's rows: set rows 4 wv .. 4 wv + 3
     const int64_t cols = a.a_cols + a.b_cols;
     const int groups = (int)(cols >> 4);
     const int g0 = blockIdx.x * kTiledGroups;
@@ -179,14 +182,14 @@ __global__ __launch_bounds__(64) void token_cat_fp4_tiled_kernel(TokenCatArgs a)
     bool ok[kTiledLoads];
 #pragma unroll
     for (int t = 0; t < kTiledLoads; ++t) {
-        const int sr = t * kTiledRowsPerLoad + lane / kTiledLanesPerRow;
+        const int sr = (wv * kTiledLoads + t) * kTiledRowsPerLoad + lane / kTiledLanesPerRow;
         const int64_t row = m0 + 32 * (sr >> 3) + (sr & 7);
         ok[t] = row < a.rows && g < groups;
         raw[t] = ok[t] ? stream_load16(cat_source(a, row, g) + 8 * half) : (u32x4){0, 0, 0, 0};
     }
 #pragma unroll
     for (int t = 0; t < kTiledLoads; ++t) {
-        const int sr = t * kTiledRowsPerLoad + lane / kTiledLanesPerRow;
+        const int sr = (wv * kTiledLoads + t) * kTiledRowsPerLoad + lane / kTiledLanesPerRow;
         const int64_t row = m0 + 32 * (sr >> 3) + (sr & 7);
         float f[8];
         unpack8(raw[t], f);
@@ -213,9 +216,7 @@ __global__ __launch_bounds__(64) void token_cat_fp4_tiled_kernel(TokenCatArgs a)
     __syncthreads();
     // Dword d of the line of tile column kc holds the scales of groups
     // 4 kc .. 4 kc + 3 of set row 8 (d % 4) + d / 4.
-#pragma unroll
-    for (int n = 0; n < kTiledCols / 2; ++n) {
-        const int idx = n * 64 + lane;
+    for (int idx = (int)threadIdx.x; idx < kTiledCols * 32; idx += 64 * kTiledSetWaves) {
         const int kc = idx >> 5, d = idx & 31;
         const int gc = g0 + 4 * kc;
         if (gc < groups) {
@@ -272,8 +273,8 @@ hipError_t launch_token_cat_fp4(const TokenCatArgs& a, hipStream_t stream) {
             b.out = a.out + set0 * 32 * ((a.a_cols + a.b_cols) / 2);
             b.out_scales = a.out_scales + set0 * 32 * groups;
             b.rows = a.rows - set0 * 32;
-            hipLaunchKernelGGL(token_cat_fp4_tiled_kernel, dim3((unsigned)chunks, (unsigned)n), dim3(64),
-                               0, stream, b);
+            hipLaunchKernelGGL(token_cat_fp4_tiled_kernel, dim3((unsigned)chunks, (unsigned)n),
+                               dim3(64 * kTiledSetWaves), 0, stream, b);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

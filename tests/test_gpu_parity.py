@@ -536,9 +536,9 @@ def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed
 
 FP4_128X4_CASES = [
     (4608, 6144, 18432, 50),  # FLUX.2 single block
-    (130, 64, 192, 51),       # 16 groups: one wave's four tile columns; two row tiles
-    (33, 64, 128, 52),        # 12 groups: a wave with three of its four tile columns
-    (300, 1024, 1088, 53),    # 132 groups: the last wave holds one tile column; three row tiles
+    (130, 64, 192, 51),       # 16 groups: one workgroup's four tile columns; two row tiles
+    (33, 64, 128, 52),        # 12 groups: a workgroup with three of its four tile columns
+    (300, 1024, 1088, 53),    # 132 groups: the last workgroup holds one tile column; three row tiles
     (129, 6144, 64, 54),      # 388 groups, the branch boundary inside a wave's span
 ]
 
