@@ -8,10 +8,11 @@
 // epsilon, rotated by interleaved (non-NeoX) RoPE from an fp32 cache, V is
 // copied, and all three are written in [text, image] order.
 //
-// Layout on gfx950: one wave64 per (joint token, part in {Q, K, V}, group of
-// kPasses * 4 heads). The wave is four 16-lane rows; row r takes heads r,
-// r + 4, ... of its group, and lane s of a row holds elements 8s..8s+7 of its
-// head (one 16-byte load). A head's sum of squares is a 16-lane DPP
+// Layout on gfx950: one wave64 per (joint token, part in {Q, K}, group of
+// kPasses * 4 heads), and one per (joint token, group of 4 heads) for the V
+// copy. The wave is four 16-lane rows; row r takes heads r, r + 4, ... of its
+// group, and lane s of a row holds elements 8s..8s+7 of its head (one 16-byte
+// load). A head's sum of squares is a 16-lane DPP
 // reduction, the RoPE pairs (2i, 2i+1) sit inside one lane, and the lane's
 // four cos/sin values are loaded once per wave.
 //
@@ -70,27 +71,46 @@ __device__ __forceinline__ void rope_pack8(const float (&n)[8], const float (&cs
     }
 }
 
-// kPasses 4-head passes per wave (a wave covers 4 * kPasses heads); a token
-// has kHBlocks such head groups. Grid: x = unit, y = part, one wave per
-// workgroup; unit u of a part is head group u % kHBlocks of joint token
-// u / kHBlocks, so consecutive waves read consecutive memory. One-wave
-// workgroups are dispatched and retired independently; on MI355X they ran
-// this shape 1.5% faster than four-wave workgroups. Everything derived from
-// the workgroup index (token, stream, source and weight pointers) is
-// wave-uniform and lives in scalar registers: the pointers come from scalar
-// loads of the argument block, so the streaming loads issue without waiting
-// on per-lane loads.
+// kPasses 4-head passes per Q/K wave (a wave covers 4 * kPasses heads); a
+// token has kHBlocks such head groups, and a unit is one of them. One wave per
+// workgroup; the 1-D grid holds the Q units, then the K units, then kPasses V
+// waves per unit, each copying one 4-head pass (a single 16-byte chunk per
+// lane, the form a plain copy streams best in: 2.5% faster over the launch
+// than V waves of 4 * kPasses heads). Unit u is head group u % kHBlocks of
+// joint token u / kHBlocks, so consecutive waves read consecutive memory.
+// One-wave workgroups are dispatched and retired independently; on MI355X
+// they ran this shape 1.5% faster than four-wave workgroups. Everything
+// derived from the workgroup index (token, stream, source and weight
+// pointers) is wave-uniform and lives in scalar registers: the pointers come
+// from scalar loads of the argument block, so the streaming loads issue
+// without waiting on per-lane loads.
 template <int kPasses, int kHBlocks>
 __global__ __launch_bounds__(64) void qkv_epilogue_kernel(QkvArgs a) {
     constexpr int kHeadsPerWave = 4 * kPasses;
     const int lane = threadIdx.x;
     const int r = lane >> 4;  // head slot within a pass
     const int s = lane & 15;  // 8-element slice of the head
-    const uint64_t unit = blockIdx.x;
+    const uint64_t units = (uint64_t)(a.txt_rows + a.img_rows) * kHBlocks;
+    const uint64_t b = blockIdx.x;
+    if (b >= 2 * units) {  // V: a bit copy of one 4-head pass into the joint layout
+        const uint64_t vb = b - 2 * units;
+        const uint64_t unit = vb / kPasses;
+        const int p = (int)(vb % kPasses);
+        const int64_t j = (int64_t)(unit / kHBlocks);
+        const int hb = (int)(unit % kHBlocks);
+        const bool is_txt = j < a.txt_rows;
+        const int64_t i = is_txt ? j : j - a.txt_rows;
+        const uint16_t* src = (is_txt ? a.txt[2] : a.img[2]) + i * (is_txt ? a.txt_stride : a.img_stride);
+        uint16_t* dst = a.joint[2] + j * (int64_t)a.heads * kHeadDim;
+        const int head = hb * kHeadsPerWave + 4 * p + r;
+        if (head < a.heads)
+            store16(dst + head * kHeadDim + 8 * s, stream_load16(src + head * kHeadDim + 8 * s));
+        return;
+    }
+    const int part = (int)(b / units);  // 0 = Q, 1 = K
+    const uint64_t unit = b % units;
     const int64_t j = (int64_t)(unit / kHBlocks);
     const int hb = (int)(unit % kHBlocks);
-    if (j >= a.txt_rows + a.img_rows) return;
-    const int part = blockIdx.y;  // 0 = Q, 1 = K, 2 = V
 
     const bool is_txt = j < a.txt_rows;
     const int64_t i = is_txt ? j : j - a.txt_rows;
@@ -108,13 +128,6 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(QkvArgs a) {
         head[p] = hb * kHeadsPerWave + 4 * p + r;
         const int hl = head[p] < a.heads ? head[p] : a.heads - 1;
         xin[p] = stream_load16(src + hl * kHeadDim + 8 * s);
-    }
-
-    if (part == 2) {  // V: bit copy into the joint layout
-#pragma unroll
-        for (int p = 0; p < kPasses; ++p)
-            if (head[p] < a.heads) store16(dst + head[p] * kHeadDim + 8 * s, xin[p]);
-        return;
     }
 
     float w[8];
@@ -153,9 +166,10 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(QkvArgs a) {
 template <int kPasses, int kHBlocks>
 hipError_t launch_groups(const QkvArgs& a, hipStream_t stream) {
     const uint64_t units = (uint64_t)(a.txt_rows + a.img_rows) * kHBlocks;
-    if (units * 64 >= kMaxGridLanes) return kGridTooLarge;
-    hipLaunchKernelGGL((qkv_epilogue_kernel<kPasses, kHBlocks>), dim3((unsigned)units, 3), dim3(64),
-                       0, stream, a);
+    const uint64_t blocks = units * (2 + kPasses);  // Q and K units, then kPasses V waves per unit
+    if (blocks * 64 >= kMaxGridLanes) return kGridTooLarge;
+    hipLaunchKernelGGL((qkv_epilogue_kernel<kPasses, kHBlocks>), dim3((unsigned)blocks), dim3(64), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
