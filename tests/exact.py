@@ -6,6 +6,7 @@ This shares nothing with oracle.c, which rounds by bit-spacing arithmetic.
 """
 from __future__ import annotations
 
+from decimal import Decimal, localcontext
 from fractions import Fraction
 
 import numpy as np
@@ -93,3 +94,14 @@ def is_bf16_midpoint(x: Fraction) -> bool:
         if (v + bf16_value(bits)) / 2 == x:
             return True
     return False
+
+
+def rsqrt_nearest_f32(t: Fraction) -> np.float32:
+    """Nearest binary32 to 1 / sqrt(t) for a positive rational t. The root is
+    taken with 80 significant decimal digits (decimal module), so the result
+    is the correctly rounded one unless 1/sqrt(t) lies within 1e-79 (relative)
+    of a binary32 midpoint."""
+    with localcontext() as ctx:
+        ctx.prec = 80
+        r = Decimal(1) / (Decimal(t.numerator) / Decimal(t.denominator)).sqrt()
+    return nearest_f32(Fraction(r))

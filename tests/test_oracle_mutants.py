@@ -99,6 +99,32 @@ MUTANTS = {
     "residual norm FP4 normalises x instead of the new residual": [
         ("oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, r_out, scale, shift, g, rows,",
          "oracle_norm_modulate_fp4(y, packed, scales, s_pre, pre, x, scale, shift, g, rows,")],
+    "RMS inverse through binary32 sqrt and division": [
+        ("return (float)(1.0 / sqrt(ms + (double)eps));",
+         "return 1.0f / sqrtf((float)(ms + (double)eps));")],
+    "RMSNorm mean of squares over n - 1": [
+        ("const double ms = ss / (double)n;", "const double ms = ss / (double)(n - 1);")],
+    "RMSNorm weight applied to the inverse first": [
+        ("const float t = bf(x[i]) * inv;\n        scratch[i] = oracle_bf16_from_f32(t * bf(w[i]));",
+         "const float t = inv * bf(w[i]);\n        scratch[i] = oracle_bf16_from_f32(bf(x[i]) * t);")],
+    "RoPE products rounded to binary32": [
+        ("out[2 * p] = oracle_bf16_of_exact_sum(n0 * c, -(n1 * s));",
+         "out[2 * p] = oracle_bf16_of_exact_sum((float)(n0 * c), -(double)(float)(n1 * s));"),
+        ("out[2 * p + 1] = oracle_bf16_of_exact_sum(n1 * c, n0 * s);",
+         "out[2 * p + 1] = oracle_bf16_of_exact_sum((float)(n1 * c), (float)(n0 * s));")],
+    "LayerNorm sum accumulated in binary32": [
+        ("double sum = 0.0;\n    for (int64_t i = 0; i < n; ++i) sum += (double)bf(v[i]);",
+         "float sum = 0.0f;\n    for (int64_t i = 0; i < n; ++i) sum += bf(v[i]);")],
+    "modulation multiply and add rounded separately": [
+        ("const float modulated = fmaf(norm, one_plus_scale, bf(shift[j]));",
+         "const float modulated = norm * one_plus_scale + bf(shift[j]);")],
+    "FP4 scale as amax * (g / 6)": [
+        ("const float sp = (amax / 6.0f) * g;", "const float sp = amax * (g / 6.0f);")],
+    "FP4 scale as (amax * g) / 6": [
+        ("const float sp = (amax / 6.0f) * g;", "const float sp = (amax * g) / 6.0f;")],
+    "FP4 element value as (x * g) / scale": [
+        ("const float t = bf(grp[k]) * kscale;",
+         "const float t = (s8 == 0) ? 0.0f : (bf(grp[k]) * g) / (float)oracle_e4m3_decode(s8);")],
 }
 
 
