@@ -14,9 +14,11 @@ in the 256 MB Infinity Cache from the previous step.
 
 Bytes are compulsory bytes: every input read once, every output written once,
 row-broadcast vectors once. The printed JSON line reports the whole-step
-throughput (GB/s); per kernel, its mean duration launched back to back over
-rotating buffer sets (us_per_call, GB/s) and its marginal cost inside the
-step (us_in_step); the roofline entry of the kernel that takes the most
+throughput (GB/s) over exactly --steps timed steps, taken after --warmup
+untimed steps and a settling phase that keeps the GPU busy until its step
+time is steady (the spread of further timed windows is reported beside it);
+per kernel, its mean duration launched back to back over rotating buffer sets
+(us_per_call, GB/s); the roofline entry of the kernel that takes the most
 time; and the CPU oracle timed on a row sample.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--blocks N]
@@ -237,9 +239,9 @@ def time_launches(torch, fns, reps):
     return start.elapsed_time(end) / reps, wall / reps
 
 
-def time_steps(torch, wl, steps, skip=None):
-    """Mean ms per step (all launches of `wl` except `skip`, in order)."""
-    fns = [fn for n, _, fn in wl.launches if n != skip]
+def time_steps(torch, wl, steps):
+    """Mean ms per step (all launches of `wl`, in order)."""
+    fns = [fn for _, _, fn in wl.launches]
 
     def step():
         for fn in fns:
@@ -251,13 +253,30 @@ def time_steps(torch, wl, steps, skip=None):
 ROTATION_BYTES = 640 << 20  # > 2x the 256 MB Infinity Cache
 
 
-def kernel_timings(torch, qe, wl, steps, in_step=True):
-    """Per launch: (a) its mean duration when launched back to back, cycling
+SETTLE_S = 0.5       # untimed GPU work before the timed steps
+SETTLE_STEP_TOL = 0.01  # ... until two consecutive 20-step windows agree within 1%
+SPREAD_WINDOWS = 5   # timed windows of --steps steps each, after the headline one
+
+
+def settle(torch, wl):
+    """Untimed steps until the GPU has run the step for at least SETTLE_S
+    seconds and two consecutive 20-step windows agree within 1% (at most 4 s):
+    the timed steps then run at steady clocks. Returns the steps run."""
+    n, t0, prev = 0, time.perf_counter(), None
+    while True:
+        ms, _ = time_steps(torch, wl, 20)
+        n += 20
+        elapsed = time.perf_counter() - t0
+        steady = prev is not None and abs(ms - prev) <= SETTLE_STEP_TOL * prev
+        if (elapsed >= SETTLE_S and steady) or elapsed >= 4.0:
+            return n
+        prev = ms
+
+
+def kernel_timings(torch, qe, wl, steps):
+    """Per launch: its mean duration when launched back to back, cycling
     through enough independent buffer sets that the sets together exceed
-    twice the Infinity Cache (so every launch reads from HBM), and (b) its
-    marginal cost inside the step: step time minus the time of the same step
-    without it."""
-    full = time_steps(torch, wl, steps)[0] if in_step else None
+    twice the Infinity Cache (so every launch reads from HBM)."""
     out = {}
     for name, nbytes, fn in wl.launches:
         # The extra Workload objects own the buffers their launches address:
@@ -269,10 +288,9 @@ def kernel_timings(torch, qe, wl, steps, in_step=True):
         for f in sets:
             f()
         iso_ms, _ = time_launches(torch, sets, reps)
-        marg = full - time_steps(torch, wl, steps, skip=name)[0] if in_step else None
-        out[name] = {"iso_ms": iso_ms, "in_step_ms": marg, "sets": len(sets), "reps": reps}
+        out[name] = {"iso_ms": iso_ms, "sets": len(sets), "reps": reps}
         del sets, extra
-    return full, out
+    return out
 
 
 # Source files that define each launch's kernel (for matching profiled traffic).
@@ -322,6 +340,18 @@ def cpu_threads():
     except AttributeError:
         n = os.cpu_count() or 1
     return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(sample_div=2, threads=1):
@@ -390,6 +420,7 @@ def cpu_baseline(sample_div=2, threads=1):
               + bytes_cat_fp4(flux, C))
     how = "single thread" if threads == 1 else f"{threads} threads, rows cut into {threads} slices"
     return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"every epilogue of the step on 1/{sample_div} of its rows "
                       f"({img} image + {txt} text tokens, {flux} FLUX.2 rows), {how}, {secs:.1f} s"}
 
@@ -465,7 +496,7 @@ def norm_rows_timings(torch, qe, steps):
     other launch), and on one buffer set launched back to back (warm), the
     latency figure for the 127-row case."""
     wl = Workload(torch, qe, seed=0, names=tuple("norm_r%d" % r for r in NORM_ROWS))
-    _, t = kernel_timings(torch, qe, wl, steps, in_step=False)
+    t = kernel_timings(torch, qe, wl, steps)
     out = {}
     for (name, nbytes, fn), rows in zip(wl.launches, NORM_ROWS):
         iso = t[name]["iso_ms"]
@@ -571,7 +602,7 @@ def split_path_timings(torch, steps):
 def extra_timings(torch, qe, steps):
     """Isolated per-launch timings of the kernels timed beside the step."""
     ex = Workload(torch, qe, seed=0, names=Workload.EXTRA)
-    _, ext = kernel_timings(torch, qe, ex, steps, in_step=False)
+    ext = kernel_timings(torch, qe, ex, steps)
     extra = {}
     for name, nbytes, _ in ex.launches:
         iso = ext[name]["iso_ms"]
@@ -631,22 +662,28 @@ def main():
     wl = Workload(torch, qe, seed=0, names=names)
     for _ in range(args.warmup):
         wl.step()
-    ms, wall = time_steps(torch, wl, args.steps)
+    settle_steps = settle(torch, wl)
+    ms, wall = time_steps(torch, wl, args.steps)  # the headline: exactly --steps steps
     value = wl.step_bytes / (ms * 1e-3) / 1e9
+    windows = [time_steps(torch, wl, args.steps)[0] for _ in range(SPREAD_WINDOWS)]
+    spread = {"windows": SPREAD_WINDOWS, "steps_per_window": args.steps,
+              "ms_per_step": [round(w, 4) for w in windows],
+              "min_ms": round(min(windows), 4), "max_ms": round(max(windows), 4)}
     if args.step_only:
         print(json.dumps({"metric": METRIC, "value": round(value, 1), "unit": "GB/s",
-                          "ms_per_step": round(ms, 4), "steps": args.steps}), flush=True)
+                          "ms_per_step": round(ms, 4), "steps": args.steps,
+                          "settle_steps": settle_steps, "spread": spread}), flush=True)
         return
-    _, timings = kernel_timings(torch, qe, wl, args.steps)
+    timings = kernel_timings(torch, qe, wl, args.steps)
 
     kernels = {}
     for name, nbytes, _ in wl.launches:
         t = timings[name]
-        iso, marg = t["iso_ms"], t["in_step_ms"]
+        iso = t["iso_ms"]
         kernels[name] = {"us_per_call": round(1e3 * iso, 3), "bytes": nbytes,
                          "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
                          "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                         "us_in_step": round(1e3 * marg, 3), "rotation_sets": t["sets"]}
+                         "rotation_sets": t["sets"]}
         if nbytes < 32 << 20:  # short launches: also without the Python launch cost
             kernels[name]["graph_us_per_call"] = round(graph_us_per_call(torch, qe, name, nbytes), 3)
     extra = {} if args.only or args.no_extra else extra_timings(torch, qe, args.steps)
@@ -665,7 +702,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded randn, resident in HBM)",
         "config": {"workload": "Qwen-Image block epilogues (hidden 3072, 512 text + 4096 image "
                                "tokens, 24x128 heads) + FLUX.2 single-block token-cat FP8/FP4 "
@@ -674,6 +711,7 @@ def main():
                    "io": "bf16 in; bf16 + E4M3 / E2M1 out", "parallelism": "1 GPU"},
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "wall_ms_per_step": round(1e3 * wall, 4),
+        "settle_steps": settle_steps, "spread": spread,
         "kernels": kernels,
         "extra_kernels": extra,
         "norm_rows": norm_rows,

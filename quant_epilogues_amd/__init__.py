@@ -1,15 +1,19 @@
 """Fused DiT-block epilogues for MI355X (gfx950): HIP kernels behind a C ABI.
 
-The five entry points of include/dit_epilogues.h are exposed with the same
-names (``dit_*``, raw pointers and sizes, caller-allocated outputs), plus
-allocating conveniences that take and return torch device tensors:
+The entry points of include/dit_epilogues.h are exposed with the same names
+(``dit_*``, raw pointers and sizes, caller-allocated outputs), plus allocating
+conveniences that take and return torch device tensors:
 
   norm_modulate_fp8                 -> (y bf16, q e4m3 bytes)
   scale_residual_norm_modulate_fp8  -> (residual_out, y, q)
+  norm_modulate_fp4                 -> (y, FP4 packed bytes, scales)
+  scale_residual_norm_modulate_fp4  -> (residual_out, y, FP4 packed bytes, scales)
   qkv_epilogue                      -> (joint_q, joint_k, joint_v)
   bias_mul_add                      -> y
   token_cat_quant                   -> FP8 bytes, or (FP4 packed bytes, scales)
 
+The raw ``dit_*`` functions pass pointers through unchecked, as the C ABI
+does; the conveniences check every tensor's dtype, shape and device first.
 torch provides device memory and streams only; all arithmetic runs in the
 library's kernels, and nothing falls back to the CPU.
 """
@@ -27,21 +31,53 @@ from ._native import (  # noqa: F401
 )
 
 
-def _dense_bf16(t: torch.Tensor, name: str) -> None:
-    if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+# Argument checks. The C ABI takes raw pointers and cannot see sizes, so these
+# wrappers check every tensor against the sizes the kernels will read or write,
+# and that all tensors sit on one GPU, before any pointer reaches a kernel.
+# Shapes and dtypes are checked first, the device last.
+
+def _bf16(t, name: str, shape=None) -> torch.Tensor:
+    """A contiguous bf16 tensor, of `shape` if given."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a bf16 tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
 
 
-def _scalar_f32(t: torch.Tensor, name: str) -> None:
-    if t.dtype != torch.float32 or t.numel() != 1 or not t.is_cuda:
-        raise ValueError(f"{name} must be a one-element fp32 device tensor")
+def _scalar_f32(t, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != 1:
+        raise ValueError(f"{name} must be a one-element fp32 tensor")
+    return t
 
 
-def _outputs(x, want_y, want_q, input_scale):
+def _one_gpu(*tensors) -> None:
+    """Every given tensor (None skipped) on one and the same GPU."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError("all tensors must be on one GPU (one cuda device)")
+
+
+def _rows_hidden(x, name: str = "x"):
+    _bf16(x, name)
+    if x.dim() < 1 or x.shape[-1] == 0:
+        raise ValueError(f"{name} must have a non-empty last dimension")
+    return x.numel() // x.shape[-1], x.shape[-1]
+
+
+def _residual_args(x, bias, gate, residual, scale, shift, hidden) -> None:
+    _bf16(residual, "residual", x.shape)
+    for t, n in ((gate, "gate"), (scale, "scale"), (shift, "shift")):
+        _bf16(t, n, (hidden,))
+    if bias is not None:
+        _bf16(bias, "bias", (hidden,))
+
+
+def _outputs(x, want_y, want_q):
     if not (want_y or want_q):
         raise ValueError("at least one of the bf16 and FP8 outputs must be requested")
-    if want_q:
-        _scalar_f32(input_scale, "input_scale")
     y = torch.empty_like(x) if want_y else None
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if want_q else None
     return y, q
@@ -51,13 +87,15 @@ def norm_modulate_fp8(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
                       input_scale: torch.Tensor | None, eps: float = 1e-6,
                       want_y: bool = True, want_q: bool = True):
     """LayerNorm (no affine) + AdaLN scale/shift + static FP8: returns (y, q);
-    an output not asked for is None (and not written)."""
-    for t, n in ((x, "x"), (scale, "scale"), (shift, "shift")):
-        _dense_bf16(t, n)
-    hidden = x.shape[-1]
-    y, q = _outputs(x, want_y, want_q, input_scale)
-    dit_norm_modulate_fp8(y, q, x, scale, shift, input_scale if want_q else None,
-                          x.numel() // hidden, hidden, eps)
+    an output not asked for is None (and not written). x is [..., hidden];
+    scale and shift are [hidden]; input_scale is a one-element fp32 tensor."""
+    rows, hidden = _rows_hidden(x)
+    _bf16(scale, "scale", (hidden,))
+    _bf16(shift, "shift", (hidden,))
+    s = _scalar_f32(input_scale, "input_scale") if want_q else None
+    _one_gpu(x, scale, shift, s)
+    y, q = _outputs(x, want_y, want_q)
+    dit_norm_modulate_fp8(y, q, x, scale, shift, s, rows, hidden, eps)
     return y, q
 
 
@@ -65,23 +103,20 @@ def scale_residual_norm_modulate_fp8(x, bias, gate, residual, scale, shift, inpu
                                      eps: float = 1e-6, want_y: bool = True,
                                      want_q: bool = True):
     """bias (optional) + gated residual, then norm/modulate/FP8:
-    returns (residual_out, y, q); an output not asked for is None."""
-    for t, n in ((x, "x"), (gate, "gate"), (residual, "residual"), (scale, "scale"),
-                 (shift, "shift")):
-        _dense_bf16(t, n)
-    if bias is not None:
-        _dense_bf16(bias, "bias")
-    hidden = x.shape[-1]
+    returns (residual_out, y, q); an output not asked for is None. x and
+    residual are [..., hidden]; bias, gate, scale and shift are [hidden]."""
+    rows, hidden = _rows_hidden(x)
+    _residual_args(x, bias, gate, residual, scale, shift, hidden)
+    s = _scalar_f32(input_scale, "input_scale") if want_q else None
+    _one_gpu(x, bias, gate, residual, scale, shift, s)
     r = torch.empty_like(x)
-    y, q = _outputs(x, want_y, want_q, input_scale)
-    dit_scale_residual_norm_modulate_fp8(r, y, q, x, bias, gate, residual, scale, shift,
-                                         input_scale if want_q else None,
-                                         x.numel() // hidden, hidden, eps)
+    y, q = _outputs(x, want_y, want_q)
+    dit_scale_residual_norm_modulate_fp8(r, y, q, x, bias, gate, residual, scale, shift, s,
+                                         rows, hidden, eps)
     return r, y, q
 
 
-def _fp4_outputs(x):
-    rows, hidden = x.numel() // x.shape[-1], x.shape[-1]
+def _fp4_outputs(x, rows, hidden):
     packed = torch.empty((rows, hidden // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty(((rows + 127) // 128 * 128, hidden // 16), dtype=torch.uint8,
                          device=x.device)
@@ -93,14 +128,15 @@ def norm_modulate_fp4(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
                       scale_layout: int = DIT_FP4_SCALES_ROW_MAJOR):
     """LayerNorm (no affine) + AdaLN scale/shift + 16-element-group FP4: returns
     (y or None, packed [rows, hidden/2], scales [round_up(rows,128), hidden/16])."""
-    for t, n in ((x, "x"), (scale, "scale"), (shift, "shift")):
-        _dense_bf16(t, n)
+    rows, hidden = _rows_hidden(x)
+    _bf16(scale, "scale", (hidden,))
+    _bf16(shift, "shift", (hidden,))
     _scalar_f32(global_scale, "global_scale")
-    hidden = x.shape[-1]
+    _one_gpu(x, scale, shift, global_scale)
     y = torch.empty_like(x) if want_y else None
-    packed, scales = _fp4_outputs(x)
+    packed, scales = _fp4_outputs(x, rows, hidden)
     dit_norm_modulate_fp4(y, packed, scales, scale_layout, x, scale, shift, global_scale,
-                          x.numel() // hidden, hidden, eps)
+                          rows, hidden, eps)
     return y, packed, scales
 
 
@@ -109,25 +145,23 @@ def scale_residual_norm_modulate_fp4(x, bias, gate, residual, scale, shift, glob
                                      scale_layout: int = DIT_FP4_SCALES_ROW_MAJOR):
     """bias (optional) + gated residual, then norm/modulate/FP4: returns
     (residual_out, y or None, packed, scales)."""
-    for t, n in ((x, "x"), (gate, "gate"), (residual, "residual"), (scale, "scale"),
-                 (shift, "shift")):
-        _dense_bf16(t, n)
-    if bias is not None:
-        _dense_bf16(bias, "bias")
+    rows, hidden = _rows_hidden(x)
+    _residual_args(x, bias, gate, residual, scale, shift, hidden)
     _scalar_f32(global_scale, "global_scale")
-    hidden = x.shape[-1]
+    _one_gpu(x, bias, gate, residual, scale, shift, global_scale)
     r = torch.empty_like(x)
     y = torch.empty_like(x) if want_y else None
-    packed, scales = _fp4_outputs(x)
+    packed, scales = _fp4_outputs(x, rows, hidden)
     dit_scale_residual_norm_modulate_fp4(r, y, packed, scales, scale_layout, x, bias, gate,
-                                         residual, scale, shift, global_scale,
-                                         x.numel() // hidden, hidden, eps)
+                                         residual, scale, shift, global_scale, rows, hidden,
+                                         eps)
     return r, y, packed, scales
 
 
-def _row_view(t: torch.Tensor, width: int, name: str) -> int:
+def _row_view(t, width: int, name: str) -> int:
     """Row stride (elements) of a [rows, width] bf16 view with unit column stride."""
-    if t.dtype != torch.bfloat16 or t.dim() != 2 or t.shape[1] != width or t.stride(1) != 1:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2 \
+            or t.shape[1] != width or t.stride(1) != 1:
         raise ValueError(f"{name} must be a [rows, {width}] bf16 view with unit column stride")
     return t.stride(0)
 
@@ -139,57 +173,73 @@ def qkv_epilogue(img_q, img_k, img_v, txt_q, txt_k, txt_v, img_q_w, img_k_w, txt
     img_*/txt_* are [rows, heads * head_dim] views (e.g. column slices of the
     packed QKV GEMM output). The four fp32 cos/sin tables are [rows, head_dim/2]
     views sharing one row stride (dense tables, or column halves of one
-    [cos | sin] cache). Returns (joint_q, joint_k, joint_v), each
-    [txt_rows + img_rows, heads, head_dim]."""
+    [cos | sin] cache), with at least as many rows as their stream. Returns
+    (joint_q, joint_k, joint_v), each [txt_rows + img_rows, heads, head_dim]."""
     width = heads * head_dim
     img_stride = _row_view(img_q, width, "img_q")
     txt_stride = _row_view(txt_q, width, "txt_q")
-    for t, n, st in ((img_k, "img_k", img_stride), (img_v, "img_v", img_stride),
-                     (txt_k, "txt_k", txt_stride), (txt_v, "txt_v", txt_stride)):
-        if _row_view(t, width, n) != st:
-            raise ValueError(f"{n} must share its stream's row stride")
-    tables = [t for t, rows in ((img_cos, img_q.shape[0]), (img_sin, img_q.shape[0]),
-                                (txt_cos, txt_q.shape[0]), (txt_sin, txt_q.shape[0])) if rows]
-    for t in tables:
-        if t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1 or t.shape[1] != head_dim // 2:
-            raise ValueError("cos/sin tables must be fp32 [rows, head_dim/2] row views")
-    rope_stride = tables[0].stride(0) if tables else head_dim // 2
-    if any(t.stride(0) != rope_stride for t in tables):
+    n_img, n_txt = img_q.shape[0], txt_q.shape[0]
+    for t, n, st, rows in ((img_k, "img_k", img_stride, n_img), (img_v, "img_v", img_stride, n_img),
+                           (txt_k, "txt_k", txt_stride, n_txt), (txt_v, "txt_v", txt_stride, n_txt)):
+        if _row_view(t, width, n) != st or t.shape[0] != rows:
+            raise ValueError(f"{n} must have its stream's rows and row stride")
+    for w, n in ((img_q_w, "img_q_w"), (img_k_w, "img_k_w"), (txt_q_w, "txt_q_w"),
+                 (txt_k_w, "txt_k_w")):
+        _bf16(w, n, (head_dim,))
+    tables = [(t, n, rows) for t, n, rows in
+              ((img_cos, "img_cos", n_img), (img_sin, "img_sin", n_img),
+               (txt_cos, "txt_cos", n_txt), (txt_sin, "txt_sin", n_txt)) if rows]
+    for t, n, rows in tables:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2 \
+                or t.stride(1) != 1 or t.shape[1] != head_dim // 2:
+            raise ValueError(f"{n} must be an fp32 [rows, head_dim/2] row view")
+        if t.shape[0] < rows:
+            raise ValueError(f"{n} has {t.shape[0]} rows, its stream has {rows}")
+    rope_stride = tables[0][0].stride(0) if tables else head_dim // 2
+    if any(t.stride(0) != rope_stride for t, _, _ in tables):
         raise ValueError("the cos/sin tables must share one row stride")
-    n_tok = img_q.shape[0] + txt_q.shape[0]
-    out = [torch.empty((n_tok, heads, head_dim), dtype=torch.bfloat16, device=img_q.device)
-           for _ in range(3)]
-    dit_qkv_epilogue(out[0], out[1], out[2], img_q, img_k, img_v, img_q.shape[0], img_stride,
-                     txt_q, txt_k, txt_v, txt_q.shape[0], txt_stride, img_q_w, img_k_w,
+    _one_gpu(img_q, img_k, img_v, txt_q, txt_k, txt_v, img_q_w, img_k_w, txt_q_w, txt_k_w,
+             *(t for t, _, _ in tables))
+    out = [torch.empty((n_img + n_txt, heads, head_dim), dtype=torch.bfloat16,
+                       device=img_q.device) for _ in range(3)]
+    dit_qkv_epilogue(out[0], out[1], out[2], img_q, img_k, img_v, n_img, img_stride,
+                     txt_q, txt_k, txt_v, n_txt, txt_stride, img_q_w, img_k_w,
                      txt_q_w, txt_k_w, img_cos, img_sin, txt_cos, txt_sin, rope_stride, heads,
                      head_dim, img_eps, txt_eps)
     return tuple(out)
 
 
 def bias_mul_add(x, bias, gate, residual):
-    """y = (x + bias) * gate + residual with one bf16 rounding of the multiply-add."""
-    for t, n in ((x, "x"), (gate, "gate"), (residual, "residual")):
-        _dense_bf16(t, n)
+    """y = (x + bias) * gate + residual with one bf16 rounding of the multiply-add.
+    x and residual are [..., hidden]; bias (optional) and gate are [hidden]."""
+    rows, hidden = _rows_hidden(x)
+    _bf16(residual, "residual", x.shape)
+    _bf16(gate, "gate", (hidden,))
     if bias is not None:
-        _dense_bf16(bias, "bias")
-    hidden = x.shape[-1]
+        _bf16(bias, "bias", (hidden,))
+    _one_gpu(x, bias, gate, residual)
     y = torch.empty_like(x)
-    dit_bias_mul_add(y, x, bias, gate, residual, x.numel() // hidden, hidden)
+    dit_bias_mul_add(y, x, bias, gate, residual, rows, hidden)
     return y
 
 
 def token_cat_quant(kind: int, a: torch.Tensor, b: torch.Tensor | None,
                     scale: torch.Tensor):
-    """Quantise the row concatenation [a | b]. FP8: returns the E4M3 bytes
-    [rows, cols]. FP4: returns (packed [rows, cols/2], scales
-    [round_up(rows, 128), cols/16]); `scale` is then the global inverse scale.
-    With DIT_QUANT_FP4_E2M1_128X4 the scales buffer holds the same bytes in the
-    128x4 tile layout."""
-    _dense_bf16(a, "a")
-    if b is not None:
-        _dense_bf16(b, "b")
-    _scalar_f32(scale, "scale")
+    """Quantise the row concatenation [a | b] (a [rows, a_cols], b [rows, b_cols]
+    or None). FP8: returns the E4M3 bytes [rows, cols]. FP4: returns (packed
+    [rows, cols/2], scales [round_up(rows, 128), cols/16]); `scale` is then the
+    global inverse scale. With DIT_QUANT_FP4_E2M1_128X4 the scales buffer holds
+    the same bytes in the 128x4 tile layout."""
+    _bf16(a, "a")
+    if a.dim() != 2:
+        raise ValueError("a must be [rows, a_cols]")
     rows, a_cols = a.shape
+    if b is not None:
+        _bf16(b, "b")
+        if b.dim() != 2 or b.shape[0] != rows:
+            raise ValueError(f"b must be [{rows}, b_cols], got {tuple(b.shape)}")
+    _scalar_f32(scale, "scale")
+    _one_gpu(a, b, scale)
     b_cols = 0 if b is None else b.shape[1]
     cols = a_cols + b_cols
     if kind == DIT_QUANT_FP8_E4M3:

@@ -9,7 +9,9 @@ Rules (all outputs):
     the two codes (+0 == -0);
   * FP4 group scales: the same rule on the scale's pre-rounding value; for such
     a group the element codes are re-derived from the GPU's scale.
-Each check returns the fraction of outputs that are bit-identical.
+Each check returns the fraction of outputs that are bit-identical. With
+exact=True it also requires every output to be bit-identical (after the
+tolerance rule has been checked, so a failure says which bar was missed).
 """
 from __future__ import annotations
 
@@ -24,7 +26,14 @@ def _bf16_ulp(v: np.ndarray) -> np.ndarray:
     return 2.0 ** (e - 7)
 
 
-def check_bf16(name: str, gpu: np.ndarray, ref: np.ndarray) -> float:
+def _require_exact(name: str, gpu: np.ndarray, ref: np.ndarray, exact: bool) -> None:
+    """exact=True: every output bit pattern equal (the sign of a zero included)."""
+    if exact:
+        n_diff = int(np.count_nonzero(gpu.reshape(-1) != ref.reshape(-1)))
+        assert n_diff == 0, f"{name}: within tolerance but {n_diff} of {gpu.size} outputs differ"
+
+
+def check_bf16(name: str, gpu: np.ndarray, ref: np.ndarray, exact: bool = False) -> float:
     assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
     d = bf16_ulp_distance(gpu.reshape(-1), ref.reshape(-1))
     if d.size == 0:
@@ -33,6 +42,7 @@ def check_bf16(name: str, gpu: np.ndarray, ref: np.ndarray) -> float:
     within1 = float((d <= 1).mean())
     assert worst <= 2, f"{name}: max bf16 distance {worst} ulp"
     assert within1 >= 0.9999, f"{name}: only {within1:.6f} within 1 ulp"
+    _require_exact(name, gpu, ref, exact)
     return float((d == 0).mean())
 
 
@@ -53,7 +63,7 @@ def _e4m3_value(c: np.ndarray, table: np.ndarray) -> np.ndarray:
 
 
 def check_fp8(name: str, gpu: np.ndarray, ref: np.ndarray, pre: np.ndarray,
-              e4m3_table: np.ndarray) -> float:
+              e4m3_table: np.ndarray, exact: bool = False) -> float:
     """e4m3_table: value of each of the 256 codes (from the oracle's decoder)."""
     assert gpu.shape == ref.shape == pre.shape, name
     g, r, p = gpu.reshape(-1), ref.reshape(-1), pre.reshape(-1)
@@ -64,6 +74,7 @@ def check_fp8(name: str, gpu: np.ndarray, ref: np.ndarray, pre: np.ndarray,
         boundary = 0.5 * (_e4m3_value(g[diff], e4m3_table) + _e4m3_value(r[diff], e4m3_table))
         near = np.abs(p[diff].astype(np.float64) - boundary) <= _bf16_ulp(p[diff])
         assert np.all(near), f"{name}: {int((~near).sum())} FP8 codes differ away from a boundary"
+    _require_exact(name, gpu, ref, exact)
     return float(1.0 - diff.size / max(g.size, 1))
 
 
@@ -86,8 +97,10 @@ def _e2m1_value(n: np.ndarray) -> np.ndarray:
 
 
 def check_fp4(name: str, gpu_packed, gpu_scales, ref_packed, ref_scales, s_pre, pre,
-              x_f32: np.ndarray, g: float, e4m3_table: np.ndarray, e2m1_encode) -> tuple:
-    """Returns (exact fraction of codes, exact fraction of scales)."""
+              x_f32: np.ndarray, g: float, e4m3_table: np.ndarray, e2m1_encode,
+              exact: bool = False) -> tuple:
+    """Returns (exact fraction of codes, exact fraction of scales). Codes are
+    compared as values: +0 and -0 (0x0 and 0x8) are equal."""
     rows = ref_packed.shape[0]
     groups = ref_scales.shape[1]
     # Pad rows of the scale matrix must be exactly zero.
@@ -121,4 +134,6 @@ def check_fp4(name: str, gpu_packed, gpu_scales, ref_packed, ref_scales, s_pre, 
         p = exp_pre[diff].astype(np.float64)
         near = np.abs(np.abs(p) - np.abs(boundary)) <= _bf16_ulp(p)
         assert np.all(near), f"{name}: {int((~near).sum())} FP4 codes differ away from a boundary"
+    _require_exact(name + " scales", gpu_scales[:rows], ref_scales[:rows], exact)
+    _require_exact(name + " codes", np.asarray(gpu_packed), np.asarray(ref_packed), exact)
     return float(1.0 - diff.mean()), float(1.0 - sdiff.mean())

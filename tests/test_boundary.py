@@ -240,3 +240,67 @@ def test_token_cat_tiled_scales_need_whole_tiles(native):
     assert f(tiled, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, 0, FAKE, None) == native.DIT_OK
     assert f(tiled, FAKE, FAKE + 8, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_ALIGN
     assert f(3, FAKE, FAKE, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_UNSUPPORTED
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, json, sys
+sys.path.insert(0, sys.argv[1])
+count = ctypes.c_int(0)
+rc = ctypes.CDLL("libamdhip64.so").hipGetDeviceCount(ctypes.byref(count))
+if rc == 0 and count.value > 0:  # a device is visible: never pass it fake addresses
+    print(json.dumps({"device_visible": True}))
+    sys.exit(0)
+from quant_epilogues_amd import _native as nat
+L = nat.lib()
+F, F2 = 0x7F0000000000, 0x7F0000100000
+calls = {
+    "dit_norm_modulate_fp8": lambda: L.dit_norm_modulate_fp8(F, F, F, F, F, F, 4, 3072, 1e-6, None),
+    "dit_scale_residual_norm_modulate_fp8": lambda: L.dit_scale_residual_norm_modulate_fp8(
+        *([F] * 10 + [4, 3072, 1e-6, None])),
+    "dit_norm_modulate_fp4": lambda: L.dit_norm_modulate_fp4(
+        F, F, F, nat.DIT_FP4_SCALES_ROW_MAJOR, F, F, F, F, 4, 3072, 1e-6, None),
+    "dit_scale_residual_norm_modulate_fp4": lambda: L.dit_scale_residual_norm_modulate_fp4(
+        *([F] * 4 + [nat.DIT_FP4_SCALES_128X4] + [F] * 7 + [4, 3072, 1e-6, None])),
+    "dit_qkv_epilogue": lambda: L.dit_qkv_epilogue(
+        F, F, F, F, F, F, 8, 9216, F, F, F, 2, 9216, F, F, F, F, F, F, F, F, 64, 24, 128,
+        1e-6, 1e-6, None),
+    "dit_bias_mul_add": lambda: L.dit_bias_mul_add(F, F, F, F, F, 4, 3072, None),
+    "dit_token_cat_quant": lambda: L.dit_token_cat_quant(
+        nat.DIT_QUANT_FP4_E2M1, F, F2, F, 6144, F2, 18432, 4, F, None),
+}
+out = {}
+for name, call in calls.items():
+    status = call()
+    out[name] = [status, nat.last_error()]
+print(json.dumps({"device_visible": False, "calls": out}))
+"""
+
+
+def test_launch_failure_reports_dit_err_hip():
+    """With no GPU visible to HIP, every compute entry point passes its host
+    checks and then returns DIT_ERR_HIP with the runtime's reason: a failed
+    launch is reported, never silent. Runs in a child process whose HIP sees
+    no device; it asks HIP for the device count first and makes no call at all
+    if a device is visible."""
+    import json
+    import subprocess
+    import sys
+
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    p = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT, ROOT], env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0, p.stderr[-2000:]
+    res = json.loads(p.stdout.strip().splitlines()[-1])
+    if res["device_visible"]:
+        pytest.skip("HIP still sees a device in the child process")
+    assert set(res["calls"]) == {n for n in _native_symbols() if n not in (
+        "dit_abi_version", "dit_status_string", "dit_last_error")}
+    for name, (status, msg) in res["calls"].items():
+        assert status == 5, (name, status, msg)  # DIT_ERR_HIP
+        assert name in msg and "launch failed" in msg, (name, msg)
+
+
+def _native_symbols():
+    from quant_epilogues_amd import _native
+
+    return _native.header_symbols()

@@ -8,14 +8,52 @@ waves and workgroups, hidden sizes that are not multiples of 512, heads not
 multiples of 4 and above 24, pad rows of the FP4 scale matrix. Outputs sit
 between guard bytes that must survive every call.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
 
+import parity
 import synth
-from parity import check_bf16, check_exact, check_fp4, check_fp8
+from parity import check_exact
 
 pytestmark = pytest.mark.gpu
+
+
+# Every case below is bit-exact against the oracle. Each check first applies
+# the tolerance rule (parity.py), then requires every output byte to be
+# equal, so a failure says which of the two bars was missed.
+def check_bf16(name, gpu, ref):
+    return parity.check_bf16(name, gpu, ref, exact=True)
+
+
+def check_fp8(name, gpu, ref, pre, table):
+    return parity.check_fp8(name, gpu, ref, pre, table, exact=True)
+
+
+def check_fp4(*args):
+    return parity.check_fp4(*args, exact=True)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _row_slices(rows: int, n: int):
+    return [(rows * k // n, rows * (k + 1) // n) for k in range(n) if rows * k // n < rows * (k + 1) // n]
+
+
+def _parallel(fn, rows: int):
+    """fn(lo, hi) over contiguous row slices on a thread pool (the oracle's C
+    entry points release Python's lock); returns the results in row order."""
+    with ThreadPoolExecutor(_threads()) as ex:
+        return list(ex.map(lambda lh: fn(*lh), _row_slices(rows, 4 * _threads())))
 
 GUARD = 4096  # bytes on each side of every output buffer
 
@@ -377,21 +415,26 @@ def test_qkv_epilogue(qe, oracle_mod, img_rows, txt_rows, heads, seed, shared):
 
 def test_qkv_epilogue_flux2_full_shape(qe, oracle_mod):
     """FLUX.2 at 1024^2: 4096 image + 512 text tokens, 48 heads, one shared
-    [cos | sin] cache; the oracle checks sampled tokens of both streams."""
+    [cos | sin] cache; every token of both streams against the oracle (run on
+    row slices in parallel)."""
     _print_case("qkv_epilogue flux2", 4096, 512, 48, 11, True)
     inp = synth.qkv_inputs(4096, 512, 48, 128, seed=11, img_eps=1e-6, txt_eps=1e-6)
     gq, gk, gv = _run_qkv(qe, inp, shared_cache=True)
-    rng = np.random.default_rng(11)
-    img_sel = np.unique(np.concatenate([[0, 1, 2, 4094, 4095], rng.integers(0, 4096, 24)]))
-    txt_sel = np.unique(np.concatenate([[0, 1, 510, 511], rng.integers(0, 512, 8)]))
-    rq, rk, rv = _oracle_qkv(oracle_mod, inp, img_sel, txt_sel)
-    rows = np.concatenate([txt_sel, 512 + img_sel])
-    eq = check_bf16("joint_q", gq[rows], rq)
-    ek = check_bf16("joint_k", gk[rows], rk)
-    check_exact("joint_v", gv[rows], rv)
-    check_exact("joint_v (all rows)", gv, np.concatenate(
-        [bits(inp.txt_qkv)[:, 2 * inp.width:], bits(inp.img_qkv)[:, 2 * inp.width:]]).reshape(gv.shape))
-    print(f"exact: q {eq:.6f} k {ek:.6f}")
+    empty = np.arange(0)
+
+    def img_slice(lo, hi):
+        rq, rk, rv = _oracle_qkv(oracle_mod, inp, np.arange(lo, hi), empty)
+        sl = slice(512 + lo, 512 + hi)
+        check_bf16("joint_q", gq[sl], rq)
+        check_bf16("joint_k", gk[sl], rk)
+        check_exact("joint_v", gv[sl], rv)
+
+    rq, rk, rv = _oracle_qkv(oracle_mod, inp, empty, np.arange(512))
+    check_bf16("joint_q (text)", gq[:512], rq)
+    check_bf16("joint_k (text)", gk[:512], rk)
+    check_exact("joint_v (text)", gv[:512], rv)
+    _parallel(img_slice, 4096)
+    print("exact: q 1.000000 k 1.000000 (all 4608 tokens)")
 
 
 def test_qkv_contiguous_equals_strided(qe):
@@ -452,24 +495,19 @@ def test_bias_mul_add_tie_case(qe, oracle_mod):
 # Token concatenation + FP8 / FP4
 # ---------------------------------------------------------------------------
 
-def _sample_rows(rows, seed):
-    rng = np.random.default_rng(seed)
-    fixed = [r for r in (0, 1, 2, 127, 128, 2047, 2048, rows - 2, rows - 1) if 0 <= r < rows]
-    return np.unique(np.concatenate([fixed, rng.integers(0, rows, 24)])).astype(np.int64)
-
-
 FP8_CASES = [
-    (4608, 6144, 18432, 0.05, 0, True),  # FLUX.2 single block, sampled rows
-    (7, 96, 160, 0.05, 1, False),
-    (3, 6144, 0, 0.5, 2, False),
-    (130, 16, 48, 0.4754464328, 3, False),
-    (5, 6144, 2064, 0.05, 7, False),         # 1026 chunks: three tiles, the last ragged
-    (65540, 16, 16, 0.05, 8, False),         # rows beyond one launch's 65536
+    (4608, 6144, 18432, 0.05, 0),  # FLUX.2 single block
+    (7, 96, 160, 0.05, 1),
+    (3, 6144, 0, 0.5, 2),
+    (130, 16, 48, 0.4754464328, 3),
+    (5, 6144, 2064, 0.05, 7),         # 1026 chunks: three tiles, the last ragged
+    (65540, 16, 16, 0.05, 8),         # rows beyond one launch's 65536
 ]
 
 
-@pytest.mark.parametrize("rows,a_cols,b_cols,scale,seed,sample", FP8_CASES)
-def test_token_cat_fp8(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, scale, seed, sample):
+@pytest.mark.parametrize("rows,a_cols,b_cols,scale,seed", FP8_CASES)
+def test_token_cat_fp8(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, scale, seed):
+    """Every row against the oracle (run on row slices in parallel)."""
     _print_case("token_cat_fp8", rows, a_cols, b_cols, scale, seed)
     inp = synth.token_cat_inputs(rows, a_cols, b_cols, seed=seed, fp8_scale=scale)
     cols = a_cols + b_cols
@@ -478,10 +516,14 @@ def test_token_cat_fp8(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, scale, 
                            dev(inp.mlp) if b_cols else None, b_cols, rows, dscalar(inp.fp8_scale))
     torch.cuda.synchronize()
     out.check("out")
-    sel = _sample_rows(rows, seed) if sample else np.arange(rows)
-    a_b, m_b = bits(inp.attn)[sel], bits(inp.mlp)[sel]
-    rq, pre = oracle_mod.token_cat_fp8(a_b, m_b, inp.fp8_scale)
-    print(f"exact: q {check_fp8('q', out.bits()[sel], rq, pre, e4m3_table):.6f}")
+    got, a_b, m_b = out.bits(), bits(inp.attn), bits(inp.mlp)
+
+    def rows_check(lo, hi):
+        rq, pre = oracle_mod.token_cat_fp8(a_b[lo:hi], m_b[lo:hi], inp.fp8_scale)
+        return check_fp8(f"q rows {lo}:{hi}", got[lo:hi], rq, pre, e4m3_table)
+
+    _parallel(rows_check, rows)
+    print("exact: q 1.000000")
 
 
 @pytest.mark.parametrize("inv_scale", [1.0, 16.0, 50.0, 20.0, 2.0, 1.0 / 0.4754464328])
@@ -498,19 +540,34 @@ def test_token_cat_fp8_all_bf16_values(qe, oracle_mod, inv_scale):
 
 
 FP4_CASES = [
-    (4608, 6144, 18432, "calibrated", 0, True),
-    (17, 64, 192, "calibrated", 1, False),   # 111 pad rows in the scale matrix
-    (9, 32, 32, 1.0, 2, False),
-    (9, 32, 32, 1e4, 3, False),              # saturating scales
-    (128, 6144, 0, "calibrated", 4, False),
-    (129, 16, 16, "calibrated", 5, False),
-    (19, 4112, 4112, "calibrated", 6, False),  # 514 groups: three tiles, the last ragged
-    (65540, 16, 16, "calibrated", 7, False),   # 65664 scale rows: two launches
+    (4608, 6144, 18432, "calibrated", 0),
+    (17, 64, 192, "calibrated", 1),   # 111 pad rows in the scale matrix
+    (9, 32, 32, 1.0, 2),
+    (9, 32, 32, 1e4, 3),              # saturating scales
+    (128, 6144, 0, "calibrated", 4),
+    (129, 16, 16, "calibrated", 5),
+    (19, 4112, 4112, "calibrated", 6),  # 514 groups: three tiles, the last ragged
+    (65540, 16, 16, "calibrated", 7),   # 65664 scale rows: two launches
 ]
 
 
-@pytest.mark.parametrize("rows,a_cols,b_cols,g,seed,sample", FP4_CASES)
-def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed, sample):
+def _check_fp4_rows(oracle_mod, e4m3_table, name, packed, scales, a_b, m_b, g):
+    """Every row's codes and scales (row-major) and the pad-row scales against
+    the oracle, on row slices in parallel."""
+    rows = packed.shape[0]
+    check_exact(name + " pad scales", scales[rows:], np.zeros_like(scales[rows:]))
+
+    def rows_check(lo, hi):
+        rp, rs, s_pre, pre = oracle_mod.token_cat_fp4(a_b[lo:hi], m_b[lo:hi], g)
+        x = oracle_mod.f32_from_bf16(np.concatenate([a_b[lo:hi], m_b[lo:hi]], axis=1))
+        return check_fp4(f"{name} rows {lo}:{hi}", packed[lo:hi], scales[lo:hi], rp,
+                         rs[:hi - lo], s_pre, pre, x, g, e4m3_table, oracle_mod.e2m1_encode)
+
+    _parallel(rows_check, rows)
+
+
+@pytest.mark.parametrize("rows,a_cols,b_cols,g,seed", FP4_CASES)
+def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed):
     _print_case("token_cat_fp4", rows, a_cols, b_cols, g, seed)
     inp = synth.token_cat_inputs(rows, a_cols, b_cols, seed=seed)
     gv = inp.fp4_g if g == "calibrated" else float(np.float32(g))
@@ -522,16 +579,9 @@ def test_token_cat_fp4(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, g, seed
                            dev(inp.mlp) if b_cols else None, b_cols, rows, dscalar(gv))
     torch.cuda.synchronize()
     packed.check("packed"), scales.check("scales")
-    gp, gs = packed.bits(), scales.bits()
-    sel = _sample_rows(rows, seed) if sample else np.arange(rows)
-    a_b, m_b = bits(inp.attn)[sel], bits(inp.mlp)[sel]
-    rp, rs, s_pre, pre = oracle_mod.token_cat_fp4(a_b, m_b, gv)
-    x = oracle_mod.f32_from_bf16(np.concatenate([a_b, m_b], axis=1))
-    gs_sel = np.concatenate([gs[sel], gs[rows:]])
-    rs_full = np.concatenate([rs[:len(sel)], np.zeros((rows_pad - rows, cols // 16), np.uint8)])
-    ec, es = check_fp4("fp4", gp[sel], gs_sel, rp, rs_full, s_pre, pre, x, gv, e4m3_table,
-                       oracle_mod.e2m1_encode)
-    print(f"exact: codes {ec:.6f} scales {es:.6f}")
+    _check_fp4_rows(oracle_mod, e4m3_table, "fp4", packed.bits(), scales.bits(),
+                    bits(inp.attn), bits(inp.mlp), gv)
+    print("exact: codes 1.000000 scales 1.000000")
 
 
 FP4_128X4_CASES = [
@@ -546,8 +596,8 @@ FP4_128X4_CASES = [
 @pytest.mark.parametrize("rows,a_cols,b_cols,seed", FP4_128X4_CASES)
 def test_token_cat_fp4_128x4_scales(qe, oracle_mod, e4m3_table, rows, a_cols, b_cols, seed):
     """FP4 token concatenation with the scales in the 128x4 tile layout: the
-    packed codes equal the row-major run's and the scale bytes equal the
-    oracle's row-major scales rearranged into tiles (pad rows included)."""
+    scale bytes equal the oracle's row-major scales rearranged into tiles by
+    the oracle (pad rows included), and every row's codes equal the oracle's."""
     _print_case("token_cat_fp4 128x4", rows, a_cols, b_cols, seed)
     inp = synth.token_cat_inputs(rows, a_cols, b_cols, seed=seed)
     cols, rows_pad = a_cols + b_cols, (rows + 127) // 128 * 128
@@ -555,22 +605,23 @@ def test_token_cat_fp4_128x4_scales(qe, oracle_mod, e4m3_table, rows, a_cols, b_
     scales = Guarded((rows_pad, cols // 16), torch.uint8)
     qe.dit_token_cat_quant(qe.DIT_QUANT_FP4_E2M1_128X4, packed.t, scales.t, dev(inp.attn), a_cols,
                            dev(inp.mlp), b_cols, rows, dscalar(inp.fp4_g))
-    ref_packed, ref_scales = qe.token_cat_quant(qe.DIT_QUANT_FP4_E2M1, dev(inp.attn),
-                                                dev(inp.mlp), dscalar(inp.fp4_g))
     torch.cuda.synchronize()
     packed.check("packed"), scales.check("scales")
-    check_exact("packed", packed.bits(), ref_packed.cpu().numpy())
-    gs = ref_scales.cpu().numpy()
-    check_exact("128x4 scales", scales.bits().reshape(-1), oracle_mod.fp4_scales_to_128x4(gs))
-    # ... and the row-major run agrees with the oracle (sampled rows).
-    sel = _sample_rows(rows, seed) if rows > 1024 else np.arange(rows)
-    a_b, m_b = bits(inp.attn)[sel], bits(inp.mlp)[sel]
-    rp, rs, s_pre, pre = oracle_mod.token_cat_fp4(a_b, m_b, inp.fp4_g)
-    x = oracle_mod.f32_from_bf16(np.concatenate([a_b, m_b], axis=1))
-    rs_full = np.concatenate([rs[:len(sel)], np.zeros((rows_pad - rows, cols // 16), np.uint8)])
-    ec, es = check_fp4("fp4", packed.bits()[sel], np.concatenate([gs[sel], gs[rows:]]), rp,
-                       rs_full, s_pre, pre, x, inp.fp4_g, e4m3_table, oracle_mod.e2m1_encode)
-    print(f"exact: codes {ec:.6f} scales {es:.6f}")
+    a_b, m_b = bits(inp.attn), bits(inp.mlp)
+    ref_scales = np.zeros((rows_pad, cols // 16), np.uint8)
+
+    def rows_scales(lo, hi):
+        _, rs, _, _ = oracle_mod.token_cat_fp4(a_b[lo:hi], m_b[lo:hi], inp.fp4_g)
+        ref_scales[lo:hi] = rs[:hi - lo]
+
+    _parallel(rows_scales, rows)
+    check_exact("128x4 scales", scales.bits().reshape(-1),
+                oracle_mod.fp4_scales_to_128x4(ref_scales))
+    # The codes: the tiled scale bytes equal the oracle's (above), so the
+    # row-major comparison takes the oracle's scales as the GPU's.
+    _check_fp4_rows(oracle_mod, e4m3_table, "fp4 128x4", packed.bits(), ref_scales, a_b, m_b,
+                    inp.fp4_g)
+    print("exact: codes 1.000000 scales 1.000000")
 
 
 def test_token_cat_fp4_all_bf16_values_unit_scale(qe, oracle_mod):
