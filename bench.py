@@ -1,8 +1,7 @@
 """Benchmark of the fused DiT-block epilogues on one MI355X.
 
 One step = one pass over every fused epilogue at its full workload shape:
-  norm_img   dit_norm_modulate_fp8                 [4096, 3072]  (image tokens)
-  norm_txt   dit_norm_modulate_fp8                 [512, 3072]   (text tokens)
+  norm_dual  dit_norm_modulate_fp8_dual            [4096, 3072] image + [512, 3072] text tokens
   qkv        dit_qkv_epilogue                      512 text + 4096 image tokens, 24 x 128
   sr_norm    dit_scale_residual_norm_modulate_fp8  [4096, 3072] with bias
   bma        dit_bias_mul_add                      [4608, 3072]
@@ -84,14 +83,17 @@ def bytes_cat_fp4(rows, cols):
 class Workload:
     """Device buffers and the launch list of one step. `names` selects launches."""
 
-    ALL = ("norm_img", "norm_txt", "qkv", "sr_norm", "bma", "cat_fp8", "cat_fp4")
+    ALL = ("norm_dual", "qkv", "sr_norm", "bma", "cat_fp8", "cat_fp4")
     # Timed beside the step, not in it: the FLUX.2 shape of the QKV epilogue
     # (4096 image + 512 text tokens, 48 heads, one shared [cos | sin] cache),
     # the FP8-only LayerNorm + modulation at the FLUX.2 shape (4608 x 6144, no
     # bf16 output), the bf16-only bias + gated-residual norm (no FP8) and the
     # same norm with NVFP4 output (4096 x 3072, g = 448), and the FP4 token
     # concatenation writing its scales in the 128x4 tile layout.
-    EXTRA = ("qkv_flux2", "norm_flux2_fp8", "sr_norm_bf16", "sr_norm_fp4", "cat_fp4_128x4")
+    # The image and text norms of norm_dual as separate launches are timed
+    # beside it too.
+    EXTRA = ("qkv_flux2", "norm_flux2_fp8", "sr_norm_bf16", "sr_norm_fp4", "cat_fp4_128x4",
+             "norm_img", "norm_txt")
 
     def __init__(self, torch, qe, seed=0, names=ALL):
         import numpy as np
@@ -129,6 +131,16 @@ class Workload:
             p = P(y, q, x, sc, sh, s0625)
             return bytes_norm(rows, hidden, y=want_y), lambda: qe.dit_norm_modulate_fp8(
                 *p, rows, hidden, 1e-6, stream=st)
+
+        def norm_dual():
+            xi, sci, shi = randn(IMG, H), randn(H, std=0.1), randn(H, std=0.1)
+            xt, sct, sht = randn(TXT, H), randn(H, std=0.1), randn(H, std=0.1)
+            yi, qi = empty(IMG, H), empty(IMG, H, dtype=torch.uint8)
+            yt, qt = empty(TXT, H), empty(TXT, H, dtype=torch.uint8)
+            pi = P(yi, qi, xi, sci, shi, s0625)
+            pt = P(yt, qt, xt, sct, sht, scalar(0.02))
+            return bytes_norm(IMG, H) + bytes_norm(TXT, H), lambda: qe.dit_norm_modulate_fp8_dual(
+                *pi, IMG, 1e-6, *pt, TXT, 1e-6, H, stream=st)
 
         def qkv(heads=HEADS, shared_cache=False):
             W = heads * HEAD_DIM
@@ -199,6 +211,7 @@ class Workload:
                                                           FLUX_ROWS, pscale, stream=st)
 
         builders = {
+            "norm_dual": norm_dual,
             "norm_img": lambda: norm(IMG), "norm_txt": lambda: norm(TXT), "qkv": qkv,
             "sr_norm": sr_norm, "bma": bma,
             "cat_fp8": lambda: cat(qe.DIT_QUANT_FP8_E4M3),
@@ -295,7 +308,8 @@ def kernel_timings(torch, qe, wl, steps):
 
 # Source files that define each launch's kernel (for matching profiled traffic).
 KERNEL_SOURCES = {
-    "norm_img": "norm_modulate.hip", "norm_txt": "norm_modulate.hip", "sr_norm": "norm_modulate.hip",
+    "norm_dual": "norm_modulate.hip", "norm_img": "norm_modulate.hip",
+    "norm_txt": "norm_modulate.hip", "sr_norm": "norm_modulate.hip",
     "qkv": "qkv_epilogue.hip", "bma": "bias_mul_add.hip", "cat_fp8": "token_cat_quant.hip",
     "cat_fp4": "token_cat_quant.hip", "qkv_flux2": "qkv_epilogue.hip",
     "norm_flux2_fp8": "norm_modulate.hip", "sr_norm_bf16": "norm_modulate.hip",
@@ -425,11 +439,14 @@ def cpu_baseline(sample_div=2, threads=1):
                       f"({img} image + {txt} text tokens, {flux} FLUX.2 rows), {how}, {secs:.1f} s"}
 
 
+BLOCK_LAUNCHES = ("norm_dual", "qkv", "bma")
+
+
 def block_sequence(torch, qe, blocks, reps):
-    """Qwen-Image-shaped block sequence: per block norm-FP8 (image, text),
-    QKV epilogue, bias_mul_add, each block on its own random buffers."""
-    wls = [Workload(torch, qe, seed=100 + i, names=("norm_img", "norm_txt", "qkv", "bma"))
-           for i in range(blocks)]
+    """Qwen-Image-shaped block sequence: per block the LayerNorm + modulation +
+    FP8 of the image and text rows (one launch), the QKV epilogue and
+    bias_mul_add, each block on its own random buffers."""
+    wls = [Workload(torch, qe, seed=100 + i, names=BLOCK_LAUNCHES) for i in range(blocks)]
     for wl in wls:
         wl.step()
     torch.cuda.synchronize()
@@ -442,7 +459,8 @@ def block_sequence(torch, qe, blocks, reps):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / reps
     nbytes = sum(wl.step_bytes for wl in wls)
-    return {"blocks": blocks, "launches": 4 * blocks, "bytes": nbytes, "ms_per_pass": round(ms, 4),
+    return {"blocks": blocks, "launches": len(BLOCK_LAUNCHES) * blocks, "bytes": nbytes,
+            "ms_per_pass": round(ms, 4),
             "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
@@ -610,6 +628,8 @@ def extra_timings(torch, qe, steps):
                        "gb_s": round(nbytes / (iso * 1e-3) / 1e9, 1),
                        "pct_peak": round(100 * nbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                        "rotation_sets": ext[name]["sets"]}
+        if nbytes < 32 << 20:  # short launches: also without the Python launch cost
+            extra[name]["graph_us_per_call"] = round(graph_us_per_call(torch, qe, name, nbytes), 3)
     return extra
 
 
@@ -693,9 +713,10 @@ def main():
         log("timing the PyTorch split path ...")
         split = split_path_timings(torch, args.steps)
         for name, rec in split.items():
-            if "us_per_call" in rec:
-                rec["fused_us_per_call"] = kernels[name]["us_per_call"]
-                rec["fused_speedup"] = round(rec["us_per_call"] / kernels[name]["us_per_call"], 2)
+            fused = kernels.get(name) or extra.get(name)
+            if "us_per_call" in rec and fused:
+                rec["fused_us_per_call"] = fused["us_per_call"]
+                rec["fused_speedup"] = round(rec["us_per_call"] / fused["us_per_call"], 2)
     dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
     achieved = kernels[dom]["gb_s"]
     traffic = profiled_traffic(dom)

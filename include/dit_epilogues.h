@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 4
+#define DIT_ABI_VERSION 5
 
 typedef enum dit_status {
     DIT_OK = 0,
@@ -95,6 +95,36 @@ const char* dit_last_error(void);
 int dit_norm_modulate_fp8(void* y, uint8_t* q, const void* x, const void* scale,
                           const void* shift, const float* input_scale_dev,
                           int64_t rows, int64_t hidden, float eps, void* stream);
+
+/*
+ * dit_norm_modulate_fp8 for the two token streams of a double-stream DiT
+ * block in ONE launch: the image rows and the text rows, each with its own
+ * outputs, input, modulation vectors, FP8 input scale and epsilon, and one
+ * shared hidden size. Each stream's results are exactly those of a
+ * dit_norm_modulate_fp8 call on it alone.
+ *
+ * Defined by: sglang PR 37156 page (what each row computes, as
+ * dit_norm_modulate_fp8); sglang PR 37123 page ("Implementation breakdown"
+ * item 3: one fused kernel covers both the image and the text stream, each
+ * with its own parameters, as dit_qkv_epilogue does). Qwen-Image's 512 text
+ * rows alone leave most of the GPU idle for the launch; sharing the launch
+ * with the 4096 image rows removes that launch's fixed cost.
+ *
+ *   img_y, img_q, img_x, img_scale, img_shift, img_input_scale_dev, img_eps:
+ *       the image stream's arguments, as dit_norm_modulate_fp8 (y or q may be
+ *       NULL, not both; [img_rows, hidden] and [hidden])
+ *   txt_*   the same for the text stream
+ *   img_rows, txt_rows  >= 0 each (a stream with 0 rows needs no pointers)
+ *   hidden  shared; same limits as dit_norm_modulate_fp8 (a multiple of 8,
+ *           at most 8192)
+ */
+int dit_norm_modulate_fp8_dual(void* img_y, uint8_t* img_q, const void* img_x,
+                               const void* img_scale, const void* img_shift,
+                               const float* img_input_scale_dev, int64_t img_rows, float img_eps,
+                               void* txt_y, uint8_t* txt_q, const void* txt_x,
+                               const void* txt_scale, const void* txt_shift,
+                               const float* txt_input_scale_dev, int64_t txt_rows, float txt_eps,
+                               int64_t hidden, void* stream);
 
 /*
  * Optional input bias + gated residual, then the same LayerNorm + modulation +

@@ -5,6 +5,7 @@ The entry points of include/dit_epilogues.h are exposed with the same names
 conveniences that take and return torch device tensors:
 
   norm_modulate_fp8                 -> (y bf16, q e4m3 bytes)
+  norm_modulate_fp8_dual            -> ((img_y, img_q), (txt_y, txt_q)), one launch
   scale_residual_norm_modulate_fp8  -> (residual_out, y, q)
   norm_modulate_fp4                 -> (y, FP4 packed bytes, scales)
   scale_residual_norm_modulate_fp4  -> (residual_out, y, FP4 packed bytes, scales)
@@ -25,7 +26,7 @@ from ._native import (  # noqa: F401
     DIT_ERR_ALIGN, DIT_ERR_HIP, DIT_ERR_NULL, DIT_ERR_SHAPE, DIT_ERR_UNSUPPORTED, DIT_OK,
     DIT_FP4_SCALES_128X4, DIT_FP4_SCALES_ROW_MAJOR, DIT_QUANT_FP4_E2M1,
     DIT_QUANT_FP4_E2M1_128X4, DIT_QUANT_FP8_E4M3, LIB_PATH, DitError, dit_bias_mul_add,
-    dit_norm_modulate_fp4, dit_norm_modulate_fp8, dit_qkv_epilogue,
+    dit_norm_modulate_fp4, dit_norm_modulate_fp8, dit_norm_modulate_fp8_dual, dit_qkv_epilogue,
     dit_scale_residual_norm_modulate_fp4, dit_scale_residual_norm_modulate_fp8,
     dit_token_cat_quant, header_symbols, last_error, lib, status_string,
 )
@@ -97,6 +98,29 @@ def norm_modulate_fp8(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
     y, q = _outputs(x, want_y, want_q)
     dit_norm_modulate_fp8(y, q, x, scale, shift, s, rows, hidden, eps)
     return y, q
+
+
+def norm_modulate_fp8_dual(img_x, img_scale, img_shift, img_input_scale, txt_x, txt_scale,
+                           txt_shift, txt_input_scale, img_eps: float = 1e-6,
+                           txt_eps: float = 1e-6, want_y: bool = True, want_q: bool = True):
+    """norm_modulate_fp8 on the image rows and the text rows of a block in one
+    launch, each stream with its own modulation vectors, FP8 scale and eps:
+    returns ((img_y, img_q), (txt_y, txt_q)). Both inputs share the hidden size."""
+    img_rows, hidden = _rows_hidden(img_x, "img_x")
+    txt_rows, txt_hidden = _rows_hidden(txt_x, "txt_x")
+    if txt_hidden != hidden:
+        raise ValueError(f"txt_x must have hidden {hidden}, got {txt_hidden}")
+    for t, n in ((img_scale, "img_scale"), (img_shift, "img_shift"), (txt_scale, "txt_scale"),
+                 (txt_shift, "txt_shift")):
+        _bf16(t, n, (hidden,))
+    si = _scalar_f32(img_input_scale, "img_input_scale") if want_q else None
+    st = _scalar_f32(txt_input_scale, "txt_input_scale") if want_q else None
+    _one_gpu(img_x, txt_x, img_scale, img_shift, txt_scale, txt_shift, si, st)
+    yi, qi = _outputs(img_x, want_y, want_q)
+    yt, qt = _outputs(txt_x, want_y, want_q)
+    dit_norm_modulate_fp8_dual(yi, qi, img_x, img_scale, img_shift, si, img_rows, img_eps,
+                               yt, qt, txt_x, txt_scale, txt_shift, st, txt_rows, txt_eps, hidden)
+    return (yi, qi), (yt, qt)
 
 
 def scale_residual_norm_modulate_fp8(x, bias, gate, residual, scale, shift, input_scale,

@@ -39,6 +39,8 @@ _SIGNATURES = {
     "dit_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dit_last_error": (ctypes.c_char_p, []),
     "dit_norm_modulate_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
+    "dit_norm_modulate_fp8_dual":
+        (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _F, _P, _P, _P, _P, _P, _P, _I64, _F, _I64, _P]),
     "dit_scale_residual_norm_modulate_fp8":
         (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _P]),
     "dit_qkv_epilogue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _I64,
@@ -124,6 +126,16 @@ def dit_norm_modulate_fp8(y, q, x, scale, shift, input_scale_dev, rows, hidden, 
     _check(lib().dit_norm_modulate_fp8(_ptr(y), _ptr(q), _ptr(x), _ptr(scale), _ptr(shift),
                                        _ptr(input_scale_dev), rows, hidden, eps,
                                        _stream(stream, x)))
+
+
+def dit_norm_modulate_fp8_dual(img_y, img_q, img_x, img_scale, img_shift, img_input_scale_dev,
+                               img_rows, img_eps, txt_y, txt_q, txt_x, txt_scale, txt_shift,
+                               txt_input_scale_dev, txt_rows, txt_eps, hidden, stream=None) -> None:
+    _check(lib().dit_norm_modulate_fp8_dual(
+        _ptr(img_y), _ptr(img_q), _ptr(img_x), _ptr(img_scale), _ptr(img_shift),
+        _ptr(img_input_scale_dev), img_rows, img_eps, _ptr(txt_y), _ptr(txt_q), _ptr(txt_x),
+        _ptr(txt_scale), _ptr(txt_shift), _ptr(txt_input_scale_dev), txt_rows, txt_eps, hidden,
+        _stream(stream, img_x, txt_x)))
 
 
 def dit_scale_residual_norm_modulate_fp8(residual_out, y, q, x, bias, gate, residual, scale,

@@ -106,6 +106,55 @@ int dit_norm_modulate_fp8(void* y, uint8_t* q, const void* x, const void* scale,
     return launched(dit::launch_norm_modulate_fp8(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+// Host checks of one stream of dit_norm_modulate_fp8_dual; fills `a`.
+static int dual_stream(const char* fn, const char* which, dit::NormModulateArgs& a, void* y,
+                       uint8_t* q, const void* x, const void* scale, const void* shift,
+                       const float* input_scale_dev, int64_t rows, int64_t hidden, float eps) {
+    if (rows < 0) return fail(DIT_ERR_SHAPE, "%s: %s_rows (%lld) must be >= 0", fn, which, (long long)rows);
+    if (rows > 0 && (!x || !scale || !shift || (!y && !q) || (q && !input_scale_dev)))
+        return fail(DIT_ERR_NULL, "%s: a required %s pointer is NULL (y and q may not both be NULL; "
+                    "q needs input_scale)", fn, which);
+    if (rows > 0 && (!aligned(y, 16) || !aligned(q, 16) || !aligned(x, 16) || !aligned(scale, 16) ||
+                     !aligned(shift, 16) || !aligned(input_scale_dev, 4)))
+        return fail(DIT_ERR_ALIGN, "%s: %s tensors must be 16-byte aligned (input_scale 4-byte)", fn,
+                    which);
+    a = dit::NormModulateArgs{};
+    a.y = static_cast<uint16_t*>(y);
+    a.q = q;
+    a.x = static_cast<const uint16_t*>(x);
+    a.scale = static_cast<const uint16_t*>(scale);
+    a.shift = static_cast<const uint16_t*>(shift);
+    a.input_scale = input_scale_dev;
+    a.rows = rows;
+    a.hidden = (int32_t)hidden;
+    a.eps = eps;
+    return DIT_OK;
+}
+
+int dit_norm_modulate_fp8_dual(void* img_y, uint8_t* img_q, const void* img_x,
+                               const void* img_scale, const void* img_shift,
+                               const float* img_input_scale_dev, int64_t img_rows, float img_eps,
+                               void* txt_y, uint8_t* txt_q, const void* txt_x,
+                               const void* txt_scale, const void* txt_shift,
+                               const float* txt_input_scale_dev, int64_t txt_rows, float txt_eps,
+                               int64_t hidden, void* stream) {
+    const char* fn = "dit_norm_modulate_fp8_dual";
+    if (img_rows < 0 || txt_rows < 0)
+        return fail(DIT_ERR_SHAPE, "%s: row counts must be >= 0", fn);
+    if (int st = check_norm_shape(fn, img_rows + txt_rows, hidden)) return st;
+    dit::NormModulateArgs img, txt;
+    if (int st = dual_stream(fn, "img", img, img_y, img_q, img_x, img_scale, img_shift,
+                             img_input_scale_dev, img_rows, hidden, img_eps))
+        return st;
+    if (int st = dual_stream(fn, "txt", txt, txt_y, txt_q, txt_x, txt_scale, txt_shift,
+                             txt_input_scale_dev, txt_rows, hidden, txt_eps))
+        return st;
+    if (img_rows + txt_rows == 0) return ok();
+    clear_stale_hip_error();
+    // Text rows first, then image rows (the joint order of the QKV epilogue).
+    return launched(dit::launch_norm_modulate_fp8_dual(txt, img, static_cast<hipStream_t>(stream)), fn);
+}
+
 int dit_scale_residual_norm_modulate_fp8(void* residual_out, void* y, uint8_t* q, const void* x,
                                          const void* bias, const void* gate,
                                          const void* residual, const void* scale,

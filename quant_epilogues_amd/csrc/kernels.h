@@ -38,6 +38,10 @@ struct NormModulateArgs {
 };
 constexpr int kMaxHidden = 8192;
 hipError_t launch_norm_modulate_fp8(const NormModulateArgs& a, hipStream_t stream);
+// Two row sets of the plain LayerNorm + modulation + FP8 (no residual, no FP4)
+// with the same hidden, in one launch: a0's rows, then a1's (either may have 0).
+hipError_t launch_norm_modulate_fp8_dual(const NormModulateArgs& a0, const NormModulateArgs& a1,
+                                         hipStream_t stream);
 
 struct QkvArgs {
     uint16_t* joint[3];            // q, k, v outputs [txt + img, heads, 128]

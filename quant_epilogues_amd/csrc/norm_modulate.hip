@@ -78,18 +78,42 @@ __device__ __forceinline__ void col8(const float* cols, const NormModulateArgs& 
 // them back after the statistics instead of waiting on an L2 round trip
 // there. The registers they pass through are free again before the row is
 // converted, so occupancy stays where the streaming loads put it.
+// A launch covers one or two independent row sets (streams) that share the
+// width and the kernel instance: workgroups [0, blocks0) take the rows of a0,
+// the rest those of a1 (Qwen-Image's image and text rows, each with its own
+// modulation vectors, FP8 scale and epsilon). The choice is per workgroup, so
+// every argument read below is wave-uniform.
+// kDual instances (plain variant, FP8 output) serve such two-set launches;
+// the others ignore a1 and blocks0.
 template <int MODE, int WPR, int RPW, int V, bool kLds, bool kFp4, bool kExact, bool kHoist,
-          bool kStage>
-__global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormModulateArgs a,
-                                                                            double inv_hidden) {
+          bool kStage, bool kDual>
+__global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(
+    NormModulateArgs a0, NormModulateArgs a1, int64_t blocks0, double inv_hidden) {
     // cols: [kColVecs][hidden] fp32 = 1 + scale, shift, gate, bias
     extern __shared__ float cols[];
     __shared__ double scratch[RPW][WPR][2];
+    static_assert(!kDual || (MODE == kPlain && !kFp4), "two row sets: plain FP8 variant only");
+    NormModulateArgs sel;  // kDual: this workgroup's row set
+    if constexpr (kDual) {
+        sel = a0;
+        if ((int64_t)blockIdx.x >= blocks0) {  // the fields a plain FP8 row reads (wave-uniform)
+            sel.y = a1.y;
+            sel.q = a1.q;
+            sel.x = a1.x;
+            sel.scale = a1.scale;
+            sel.shift = a1.shift;
+            sel.input_scale = a1.input_scale;
+            sel.rows = a1.rows;
+            sel.eps = a1.eps;
+        }
+    }
+    const NormModulateArgs& a = kDual ? sel : a0;
+    const bool second = kDual && (int64_t)blockIdx.x >= blocks0;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rw = wave / WPR;  // row slot in the workgroup
     const int sw = wave % WPR;  // wave within the row
-    const int64_t row = (int64_t)blockIdx.x * RPW + rw;
+    const int64_t row = ((int64_t)blockIdx.x - (second ? blocks0 : 0)) * RPW + rw;
     const bool active = row < a.rows;  // wave-uniform; every wave still reaches the barriers
     const int H = a.hidden;
     const int cpr = H >> 3;  // chunks per row
@@ -355,30 +379,45 @@ __global__ __launch_bounds__(64 * WPR * RPW) void norm_modulate_fp8_kernel(NormM
     }
 }
 
+template <int MODE, int WPR, int RPW, int V, bool kLds, bool kFp4, bool kExact, bool kHoist,
+          bool kStage, bool kDual>
+hipError_t launch_kernel(const NormModulateArgs& a0, const NormModulateArgs& a1, int64_t blocks0,
+                         uint64_t blocks, hipStream_t stream) {
+    const int H = a0.hidden;
+    const size_t lds = kLds ? ((size_t)kColVecs<MODE> * H + (kFp4 ? 128 : 0)) * sizeof(float)
+                            : (kStage ? (size_t)WPR * 2 * V * 64 * sizeof(u32x4) : 0);
+    hipLaunchKernelGGL(
+        (norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4, kExact, kHoist, kStage, kDual>),
+        dim3((unsigned)blocks), dim3(64 * WPR * RPW), lds, stream, a0, a1, blocks0, 1.0 / (double)H);
+    return hipGetLastError();
+}
+
 // Launch with WPR waves per row, RPW rows per workgroup and V chunks per lane
 // (V * 64 * WPR >= hidden / 8); kLds stages the column vectors in LDS as fp32,
-// kStage (exact fits only) parks them raw in LDS for every row slot.
+// kStage (exact fits only) parks them raw in LDS for every row slot. a1 is the
+// second row set (a1.rows == 0: none); both share a0's width.
 template <int MODE, int WPR, int RPW, int V, bool kLds, bool kFp4, bool kHoist = false,
           bool kStage = false>
-hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
-    const int64_t grid_rows = kFp4 ? a.fp4_rows_padded : a.rows;
-    const uint64_t blocks = (uint64_t)((grid_rows + RPW - 1) / RPW);
+hipError_t launch_geom(const NormModulateArgs& a0, const NormModulateArgs& a1, hipStream_t stream) {
+    const int64_t rows0 = kFp4 ? a0.fp4_rows_padded : a0.rows;
+    const int64_t rows1 = kFp4 ? a1.fp4_rows_padded : a1.rows;
+    const int64_t blocks0 = (rows0 + RPW - 1) / RPW;
+    const uint64_t blocks = (uint64_t)(blocks0 + (rows1 + RPW - 1) / RPW);
     if (blocks * (64 * WPR * RPW) >= kMaxGridLanes) return kGridTooLarge;
-    const size_t lds = kLds ? ((size_t)kColVecs<MODE> * a.hidden + (kFp4 ? 128 : 0)) * sizeof(float)
-                            : (kStage ? (size_t)WPR * 2 * V * 64 * sizeof(u32x4) : 0);
-    const dim3 grid((unsigned)blocks), block(64 * WPR * RPW);
-    if constexpr (kStage) {  // chosen for exact fits only
-        if (a.hidden != 512 * WPR * V) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4, true, kHoist, true>),
-                           grid, block, lds, stream, a, 1.0 / (double)a.hidden);
-    } else if (MODE == kPlain && a.hidden == 512 * WPR * V) {
-        hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4, true, kHoist, false>),
-                           grid, block, lds, stream, a, 1.0 / (double)a.hidden);
-    } else {
-        hipLaunchKernelGGL((norm_modulate_fp8_kernel<MODE, WPR, RPW, V, kLds, kFp4, false, kHoist, false>),
-                           grid, block, lds, stream, a, 1.0 / (double)a.hidden);
+    const int H = a0.hidden;
+    if (kStage && H != 512 * WPR * V) return hipErrorInvalidValue;  // chosen for exact fits only
+    const bool exact = kStage || (MODE == kPlain && H == 512 * WPR * V);
+    if constexpr (MODE == kPlain && !kFp4) {
+        if (rows1 > 0)
+            return exact ? launch_kernel<MODE, WPR, RPW, V, kLds, kFp4, true, kHoist, kStage, true>(
+                               a0, a1, blocks0, blocks, stream)
+                         : launch_kernel<MODE, WPR, RPW, V, kLds, kFp4, false, kHoist, false, true>(
+                               a0, a1, blocks0, blocks, stream);
     }
-    return hipGetLastError();
+    return exact ? launch_kernel<MODE, WPR, RPW, V, kLds, kFp4, true, kHoist, kStage, false>(
+                       a0, a1, blocks0, blocks, stream)
+                 : launch_kernel<MODE, WPR, RPW, V, kLds, kFp4, false, kHoist, false, false>(
+                       a0, a1, blocks0, blocks, stream);
 }
 
 // Geometries measured on MI355X (time per call over back-to-back launches
@@ -395,22 +434,22 @@ hipError_t launch_geom(const NormModulateArgs& a, hipStream_t stream) {
 //  - residual variants, many rows: one wave per row, eight rows per workgroup,
 //    column vectors staged in LDS when they fit in 48 KiB.
 template <int MODE, bool kFp4>
-hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
+hipError_t launch_mode(const NormModulateArgs& a, const NormModulateArgs& a1, hipStream_t stream) {
     const int cpr = a.hidden / 8;
-    if (a.rows < 1024) {
+    if (a.rows + a1.rows < 1024) {
         switch ((cpr + 383) / 384) {
-            case 1: return launch_geom<MODE, 6, 1, 1, false, kFp4, true>(a, stream);
-            case 2: return launch_geom<MODE, 6, 1, 2, false, kFp4, true>(a, stream);
-            default: return launch_geom<MODE, 6, 1, 3, false, kFp4, true>(a, stream);  // up to 1152 chunks
+            case 1: return launch_geom<MODE, 6, 1, 1, false, kFp4, true>(a, a1, stream);
+            case 2: return launch_geom<MODE, 6, 1, 2, false, kFp4, true>(a, a1, stream);
+            default: return launch_geom<MODE, 6, 1, 3, false, kFp4, true>(a, a1, stream);  // up to 1152 chunks
         }
     }
     if constexpr (MODE == kPlain) {
         if (cpr > 384 && cpr <= 768) {
-            if (a.y) return launch_geom<MODE, 6, 2, 2, false, kFp4>(a, stream);
+            if (a.y) return launch_geom<MODE, 6, 2, 2, false, kFp4>(a, a1, stream);
             if constexpr (!kFp4) {
-                if (a.hidden == 512 * 4 * 3) return launch_geom<MODE, 4, 2, 3, false, kFp4, false, true>(a, stream);
+                if (a.hidden == 512 * 4 * 3) return launch_geom<MODE, 4, 2, 3, false, kFp4, false, true>(a, a1, stream);
             }
-            return launch_geom<MODE, 4, 1, 3, false, kFp4>(a, stream);
+            return launch_geom<MODE, 4, 1, 3, false, kFp4>(a, a1, stream);
         }
     }
     if constexpr (MODE != kPlain) {
@@ -419,8 +458,8 @@ hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
         switch ((cpr + 63) / 64) {
 #define DIT_NM_ONE_WAVE(VV)                                                                    \
     case VV:                                                                                   \
-        return lds ? launch_geom<MODE, 1, 8, VV, true, kFp4>(a, stream)                             \
-                   : launch_geom<MODE, 1, 8, VV, false, kFp4>(a, stream);
+        return lds ? launch_geom<MODE, 1, 8, VV, true, kFp4>(a, a1, stream)                             \
+                   : launch_geom<MODE, 1, 8, VV, false, kFp4>(a, a1, stream);
             DIT_NM_ONE_WAVE(1) DIT_NM_ONE_WAVE(2) DIT_NM_ONE_WAVE(3)
             DIT_NM_ONE_WAVE(4) DIT_NM_ONE_WAVE(5) DIT_NM_ONE_WAVE(6)
 #undef DIT_NM_ONE_WAVE
@@ -428,26 +467,38 @@ hipError_t launch_mode(const NormModulateArgs& a, hipStream_t stream) {
     }
 two_waves:
     switch ((cpr + 127) / 128) {
-        case 1: return launch_geom<MODE, 2, 4, 1, false, kFp4>(a, stream);
-        case 2: return launch_geom<MODE, 2, 4, 2, false, kFp4>(a, stream);
-        case 3: return launch_geom<MODE, 2, 4, 3, false, kFp4>(a, stream);
-        case 4: return launch_geom<MODE, 2, 4, 4, false, kFp4>(a, stream);
-        case 5: case 6: return launch_geom<MODE, 2, 4, 6, false, kFp4>(a, stream);
-        default: return launch_geom<MODE, 2, 4, 8, false, kFp4>(a, stream);  // up to 1024 chunks
+        case 1: return launch_geom<MODE, 2, 4, 1, false, kFp4>(a, a1, stream);
+        case 2: return launch_geom<MODE, 2, 4, 2, false, kFp4>(a, a1, stream);
+        case 3: return launch_geom<MODE, 2, 4, 3, false, kFp4>(a, a1, stream);
+        case 4: return launch_geom<MODE, 2, 4, 4, false, kFp4>(a, a1, stream);
+        case 5: case 6: return launch_geom<MODE, 2, 4, 6, false, kFp4>(a, a1, stream);
+        default: return launch_geom<MODE, 2, 4, 8, false, kFp4>(a, a1, stream);  // up to 1024 chunks
     }
 }
 
 template <bool kFp4>
-hipError_t launch_modes(const NormModulateArgs& a, hipStream_t stream) {
-    if (a.residual == nullptr) return launch_mode<kPlain, kFp4>(a, stream);
-    if (a.bias == nullptr) return launch_mode<kResidual, kFp4>(a, stream);
-    return launch_mode<kBiasResidual, kFp4>(a, stream);
+hipError_t launch_modes(const NormModulateArgs& a, const NormModulateArgs& a1, hipStream_t stream) {
+    if (a.residual == nullptr) return launch_mode<kPlain, kFp4>(a, a1, stream);
+    if (a.bias == nullptr) return launch_mode<kResidual, kFp4>(a, a1, stream);
+    return launch_mode<kBiasResidual, kFp4>(a, a1, stream);
 }
 
 }  // namespace
 
 hipError_t launch_norm_modulate_fp8(const NormModulateArgs& a, hipStream_t stream) {
-    return a.fp4 ? launch_modes<true>(a, stream) : launch_modes<false>(a, stream);
+    NormModulateArgs none = a;  // no second row set
+    none.rows = 0;
+    none.fp4_rows_padded = 0;
+    return a.fp4 ? launch_modes<true>(a, none, stream) : launch_modes<false>(a, none, stream);
+}
+
+// The geometry is chosen as for a0 with the two row counts added; a set with
+// no rows is left out.
+hipError_t launch_norm_modulate_fp8_dual(const NormModulateArgs& a0, const NormModulateArgs& a1,
+                                         hipStream_t stream) {
+    if (a0.rows == 0) return launch_norm_modulate_fp8(a1, stream);
+    if (a1.rows == 0) return launch_norm_modulate_fp8(a0, stream);
+    return launch_mode<kPlain, false>(a0, a1, stream);
 }
 
 }  // namespace dit

@@ -111,3 +111,15 @@ def test_qkv_checks():
         qe.qkv_epilogue(**dict(good, img_cos=cache[2:, :64]))
     with pytest.raises(ValueError, match="one GPU"):
         qe.qkv_epilogue(**good)
+
+
+def test_norm_dual_checks():
+    img, txt = z(8, H), z(2, H)
+    with pytest.raises(ValueError, match="txt_x must have hidden"):
+        qe.norm_modulate_fp8_dual(img, z(H), z(H), S, z(2, H + 8), z(H), z(H), S)
+    with pytest.raises(ValueError, match="txt_scale"):
+        qe.norm_modulate_fp8_dual(img, z(H), z(H), S, txt, z(H - 8), z(H), S)
+    with pytest.raises(ValueError, match="img_input_scale"):
+        qe.norm_modulate_fp8_dual(img, z(H), z(H), None, txt, z(H), z(H), S)
+    with pytest.raises(ValueError, match="one GPU"):
+        qe.norm_modulate_fp8_dual(img, z(H), z(H), S, txt, z(H), z(H), S)

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(native):
     declared = native.header_symbols()
     assert set(declared) == {
         "dit_abi_version", "dit_status_string", "dit_last_error", "dit_norm_modulate_fp8",
-        "dit_scale_residual_norm_modulate_fp8", "dit_norm_modulate_fp4",
+        "dit_norm_modulate_fp8_dual", "dit_scale_residual_norm_modulate_fp8", "dit_norm_modulate_fp4",
         "dit_scale_residual_norm_modulate_fp4", "dit_qkv_epilogue", "dit_bias_mul_add",
         "dit_token_cat_quant",
     }
@@ -87,6 +87,33 @@ def test_norm_modulate_refusals(native):
     assert _nm(L, s=None) == native.DIT_ERR_NULL
     assert _nm(L, y=None, rows=0) == native.DIT_OK
     assert _nm(L, q=None, s=None, rows=0) == native.DIT_OK
+
+
+def _dual(L, **kw):
+    a = dict(iy=FAKE, iq=FAKE, ix=FAKE, isc=FAKE, ish=FAKE, iss=FAKE, irows=8,
+             ty=FAKE, tq=FAKE, tx=FAKE, tsc=FAKE, tsh=FAKE, tss=FAKE, trows=2, hidden=3072)
+    a.update(kw)
+    return L.dit_norm_modulate_fp8_dual(a["iy"], a["iq"], a["ix"], a["isc"], a["ish"], a["iss"],
+                                        a["irows"], 1e-6, a["ty"], a["tq"], a["tx"], a["tsc"],
+                                        a["tsh"], a["tss"], a["trows"], 1e-5, a["hidden"], None)
+
+
+def test_norm_modulate_dual_refusals(native):
+    L = native.lib()
+    assert _dual(L, ix=None) == native.DIT_ERR_NULL
+    assert "img" in native.last_error()
+    assert _dual(L, tsc=None) == native.DIT_ERR_NULL
+    assert "txt" in native.last_error()
+    assert _dual(L, ty=None, tq=None) == native.DIT_ERR_NULL
+    assert _dual(L, iss=None) == native.DIT_ERR_NULL  # q needs its scale
+    assert _dual(L, irows=-1) == native.DIT_ERR_SHAPE
+    assert _dual(L, hidden=3076) == native.DIT_ERR_UNSUPPORTED
+    assert _dual(L, tx=FAKE + 2) == native.DIT_ERR_ALIGN
+    assert _dual(L, irows=0, trows=0) == native.DIT_OK
+    # A stream with no rows needs no pointers; the other is still checked.
+    assert _dual(L, irows=0, trows=0, ix=None, tx=None) == native.DIT_OK
+    assert _dual(L, irows=0, ix=None, iy=None, iq=None, tx=FAKE + 8) == native.DIT_ERR_ALIGN
+    assert _dual(L, irows=1 << 30) == native.DIT_ERR_UNSUPPORTED
 
 
 def test_scale_residual_refusals(native):
@@ -255,6 +282,8 @@ L = nat.lib()
 F, F2 = 0x7F0000000000, 0x7F0000100000
 calls = {
     "dit_norm_modulate_fp8": lambda: L.dit_norm_modulate_fp8(F, F, F, F, F, F, 4, 3072, 1e-6, None),
+    "dit_norm_modulate_fp8_dual": lambda: L.dit_norm_modulate_fp8_dual(
+        F, F, F, F, F, F, 8, 1e-6, F, F, F, F, F, F, 2, 1e-6, 3072, None),
     "dit_scale_residual_norm_modulate_fp8": lambda: L.dit_scale_residual_norm_modulate_fp8(
         *([F] * 10 + [4, 3072, 1e-6, None])),
     "dit_norm_modulate_fp4": lambda: L.dit_norm_modulate_fp4(

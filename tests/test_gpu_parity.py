@@ -147,6 +147,64 @@ def test_norm_modulate_fp8(qe, oracle_mod, e4m3_table, rows, hidden, input_scale
     print(f"exact: y {ey:.6f} q {eq:.6f}")
 
 
+DUAL_CASES = [
+    # (img_rows, txt_rows, hidden, img_scale, txt_scale, img_eps, txt_eps, seed)
+    (4096, 512, 3072, 0.0625, 0.02, 1e-6, 1e-5, 60),  # Qwen-Image: 4096 image + 512 text tokens
+    (1000, 30, 3072, 0.5, 0.0625, 1e-6, 0.25, 61),    # partial last workgroup in both sets
+    (600, 300, 3072, 0.02, 0.5, 1e-6, 1e-6, 62),      # under 1024 rows in all: the latency geometry
+    (9, 1030, 6144, 0.0625, 0.02, 1e-5, 1e-6, 63),    # FLUX.2 width
+    (33, 17, 1000, 0.0625, 0.5, 1e-6, 1e-6, 64),      # ragged width: 125 chunks
+    (0, 77, 3072, 0.0625, 0.02, 1e-6, 1e-6, 65),      # no image rows
+    (1030, 0, 3072, 0.0625, 0.02, 1e-6, 1e-6, 66),    # no text rows
+]
+
+
+@pytest.mark.parametrize("img_rows,txt_rows,hidden,img_s,txt_s,img_eps,txt_eps,seed", DUAL_CASES)
+def test_norm_modulate_fp8_dual(qe, oracle_mod, e4m3_table, img_rows, txt_rows, hidden, img_s,
+                                txt_s, img_eps, txt_eps, seed):
+    """Image and text rows in one launch, each with its own vectors, FP8 scale
+    and eps: each stream equals the oracle on that stream alone."""
+    _print_case("norm_modulate_fp8_dual", img_rows, txt_rows, hidden, seed)
+    img = synth.norm_modulate_inputs(img_rows, hidden, seed=seed, input_scale=img_s, eps=img_eps)
+    txt = synth.norm_modulate_inputs(txt_rows, hidden, seed=seed + 1000, input_scale=txt_s,
+                                     eps=txt_eps)
+    out = {}
+    for name, rows in (("img", img_rows), ("txt", txt_rows)):
+        out[name] = (Guarded((rows, hidden), torch.bfloat16), Guarded((rows, hidden), torch.uint8))
+    (iy, iq), (ty, tq) = out["img"], out["txt"]
+    qe.dit_norm_modulate_fp8_dual(
+        iy.t, iq.t, dev(img.x), dev(img.scale), dev(img.shift), dscalar(img.input_scale), img_rows,
+        img.eps, ty.t, tq.t, dev(txt.x), dev(txt.scale), dev(txt.shift), dscalar(txt.input_scale),
+        txt_rows, txt.eps, hidden)
+    torch.cuda.synchronize()
+    for name, inp in (("img", img), ("txt", txt)):
+        y, q = out[name]
+        y.check(name + " y"), q.check(name + " q")
+        ry, rq, pre = oracle_mod.norm_modulate_fp8(bits(inp.x), bits(inp.scale), bits(inp.shift),
+                                                   inp.input_scale, inp.eps)
+        check_bf16(name + " y", y.bits(), ry)
+        check_fp8(name + " q", q.bits(), rq, pre, e4m3_table)
+    print("exact: y 1.000000 q 1.000000 (both streams)")
+
+
+def test_norm_modulate_fp8_dual_equals_two_calls(qe):
+    """The one-launch form and two single-stream calls give the same bytes,
+    including with one output left out."""
+    img = synth.norm_modulate_inputs(512, 3072, seed=67, input_scale=0.02)
+    txt = synth.norm_modulate_inputs(128, 3072, seed=68, input_scale=0.5, eps=1e-5)
+    args = lambda i: (dev(i.x), dev(i.scale), dev(i.shift), dscalar(i.input_scale))
+    for want_y, want_q in ((True, True), (False, True), (True, False)):
+        (yi, qi), (yt, qt) = qe.norm_modulate_fp8_dual(*args(img), *args(txt), img.eps, txt.eps,
+                                                       want_y=want_y, want_q=want_q)
+        yi2, qi2 = qe.norm_modulate_fp8(*args(img), img.eps, want_y=want_y, want_q=want_q)
+        yt2, qt2 = qe.norm_modulate_fp8(*args(txt), txt.eps, want_y=want_y, want_q=want_q)
+        torch.cuda.synchronize()
+        for a, b in ((yi, yi2), (qi, qi2), (yt, yt2), (qt, qt2)):
+            assert (a is None) == (b is None)
+            if a is not None:
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 SR_CASES = [
     (4096, 3072, 0.02, True, 0),
     (4096, 3072, 0.0625, True, 1),
@@ -710,6 +768,10 @@ def test_hip_graph_capture_replays_match_eager(qe):
 
     outs = {
         "y": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
+        "dy": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
+        "dq": torch.empty(R, H, dtype=torch.uint8, device="cuda"),
+        "dy2": torch.empty(R // 2, H, dtype=torch.bfloat16, device="cuda"),
+        "dq2": torch.empty(R // 2, H, dtype=torch.uint8, device="cuda"),
         "q": torch.empty(R, H, dtype=torch.uint8, device="cuda"),
         "r": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
         "y2": torch.empty(R, H, dtype=torch.bfloat16, device="cuda"),
@@ -729,6 +791,8 @@ def test_hip_graph_capture_replays_match_eager(qe):
     def run():
         o = outs
         qe.dit_norm_modulate_fp8(o["y"], o["q"], x, sc, sh, s8, R, H, 1e-6)
+        qe.dit_norm_modulate_fp8_dual(o["dy"], o["dq"], x, sc, sh, s8, R, 1e-6, o["dy2"], o["dq2"],
+                                      res, sh, sc, g4, R // 2, 1e-5, H)
         qe.dit_scale_residual_norm_modulate_fp8(o["r"], o["y2"], o["q2"], x, bias, gate, res, sc,
                                                 sh, s8, R, H, 1e-6)
         qe.dit_scale_residual_norm_modulate_fp4(o["r4"], None, o["p4"], o["s4"],
