@@ -443,6 +443,17 @@ hipError_t launch_mode(const NormModulateArgs& a, const NormModulateArgs& a1, hi
             default: return launch_geom<MODE, 6, 1, 3, false, kFp4, true>(a, a1, stream);  // up to 1152 chunks
         }
     }
+    if constexpr (MODE == kPlain && !kFp4) {
+        // Two waves per row and four rows per workgroup hold 16 rows per CU at
+        // once (53 VGPRs, 8 waves per SIMD), 4096 rows on the 256 CUs; a
+        // launch with up to 6144 rows (Qwen-Image's 4096 image + 512 text
+        // rows) fits in one resident round with one wave per row instead (76
+        // VGPRs, 24 rows per CU): 12.9 against 15.3 us at 4608 x 3072, where
+        // a second round of workgroups would wait for the first.
+        const int64_t rows = a.rows + a1.rows;
+        if (rows > 4096 && rows <= 6144 && cpr > 320 && cpr <= 384)
+            return launch_geom<MODE, 1, 1, 6, false, kFp4>(a, a1, stream);
+    }
     if constexpr (MODE == kPlain) {
         if (cpr > 384 && cpr <= 768) {
             if (a.y) return launch_geom<MODE, 6, 2, 2, false, kFp4>(a, a1, stream);

@@ -127,6 +127,8 @@ NORM_CASES = [
     (1030, 4104, 0.5, 10),    # 513 chunks per row: a partial last wave
     (3, 8192, 0.0625, 8),     # widest supported row: 1024 threads
     (5, 8, 0.0625, 7),        # one chunk per row
+    (4608, 3072, 0.0625, 12),  # 4097..6144 rows: one wave per row, one resident round
+    (6144, 2736, 0.02, 13),    # the same geometry at its row limit, 342 chunks (ragged)
 ]
 
 
@@ -154,6 +156,7 @@ DUAL_CASES = [
     (600, 300, 3072, 0.02, 0.5, 1e-6, 1e-6, 62),      # under 1024 rows in all: the latency geometry
     (9, 1030, 6144, 0.0625, 0.02, 1e-5, 1e-6, 63),    # FLUX.2 width
     (33, 17, 1000, 0.0625, 0.5, 1e-6, 1e-6, 64),      # ragged width: 125 chunks
+    (4000, 1000, 2736, 0.5, 0.02, 1e-6, 1e-5, 69),    # one wave per row, ragged width
     (0, 77, 3072, 0.0625, 0.02, 1e-6, 1e-6, 65),      # no image rows
     (1030, 0, 3072, 0.0625, 0.02, 1e-6, 1e-6, 66),    # no text rows
 ]
