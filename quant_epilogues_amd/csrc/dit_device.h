@@ -2,13 +2,19 @@
 // bf16 / FP8 / FP4 conversions, the exactly-rounded sums the epilogues need,
 // and wave64 reductions.
 //
-// Conversions use the gfx950 conversion instructions. Each one was checked
-// exhaustively over all 2^32 fp32 inputs against software encoders written
-// from the format definitions (round to nearest even; sign kept on zero):
+// Conversions use the gfx950 conversion instructions (round to nearest even;
+// sign kept on zero):
 //   v_cvt_pk_bf16_f32          fp32 -> bf16
 //   v_cvt_pk_fp8_f32           fp32 in [-448, 448] -> OCP E4M3FN
 //   v_cvt_scalef32_pk_fp4_f32  fp32 -> E2M1 with unit scale (saturates at 6;
 //                              first source in the low nibble)
+// The helpers below that wrap them (pack_bf16, round_bf16, clamp_e4m3 +
+// pack_e4m3x4, pack_e2m1x8) are checked on the GPU against encoders written
+// from the format definitions: on every fp32 value whose upper 16 bits are
+// any finite pattern and whose lower 16 bits lie within 2 ulps of 0 or of
+// 0x8000 -- every bf16 value, every bf16 rounding midpoint, and every E4M3
+// and E2M1 rounding boundary with its neighbours, since those boundaries have
+// few significant bits -- plus 2^22 random fp32 values.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -138,10 +144,11 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 }
 
 // a / 6 (IEEE fp32, round to nearest even) for a non-negative bf16 value a
-// held in fp32: the product with RN(1/6) and one FMA correction step. Checked
-// equal to the IEEE quotient for every non-negative finite bf16 value (with
-// fp32 denormals preserved, as these kernels run); +inf passes through.
-__device__ __forceinline__ float div6_bf16(float a) {
+// held in fp32: the product with RN(1/6) and one FMA correction step. It
+// equals the IEEE quotient for every non-negative finite bf16 value (with
+// fp32 denormals preserved, as these kernels run), checked exhaustively on
+// the GPU and, compiled for the host, on the CPU; +inf passes through.
+__host__ __device__ __forceinline__ float div6_bf16(float a) {
     const float c = 0x1.555556p-3f;  // RN(1/6)
     const float q0 = a * c;
     const float q = __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), c, q0);
