@@ -459,39 +459,10 @@ def block_sequence(torch, qe, blocks, reps):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / reps
     nbytes = sum(wl.step_bytes for wl in wls)
-    del wls
-    torch.cuda.empty_cache()
-    # The same pass captured once into a HIP graph (on a side stream, as the
-    # launches name their stream) and replayed: how a denoising loop that
-    # captures its steps would issue it.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        gwls = [Workload(torch, qe, seed=100 + i, names=BLOCK_LAUNCHES) for i in range(blocks)]
-        for wl in gwls:
-            wl.step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        for wl in gwls:
-            wl.step()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(side):
-        graph.replay()  # untimed first replay
-        start.record()
-        for _ in range(reps):
-            graph.replay()
-        end.record()
-    torch.cuda.synchronize()
-    gms = start.elapsed_time(end) / reps
-    del graph, gwls
-    torch.cuda.empty_cache()
     return {"blocks": blocks, "launches": len(BLOCK_LAUNCHES) * blocks, "bytes": nbytes,
             "ms_per_pass": round(ms, 4),
             "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            "graph_ms_per_pass": round(gms, 4),
-            "graph_pct_peak": round(100 * nbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+            "pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
