@@ -274,15 +274,17 @@ SPREAD_WINDOWS = 5   # timed windows of --steps steps each, after the headline o
 def settle(torch, wl):
     """Untimed steps until the GPU has run the step for at least SETTLE_S
     seconds and two consecutive 20-step windows agree within 1% (at most 4 s):
-    the timed steps then run at steady clocks. Returns the steps run."""
-    n, t0, prev = 0, time.perf_counter(), None
+    the timed steps then run at steady clocks. Returns the steps run and the
+    ms per step of the first 8 and the last 2 windows (the warm-up ramp)."""
+    n, t0, prev, trace = 0, time.perf_counter(), None, []
     while True:
         ms, _ = time_steps(torch, wl, 20)
+        trace.append(round(ms, 4))
         n += 20
         elapsed = time.perf_counter() - t0
         steady = prev is not None and abs(ms - prev) <= SETTLE_STEP_TOL * prev
         if (elapsed >= SETTLE_S and steady) or elapsed >= 4.0:
-            return n
+            return n, trace[:8] + (trace[-2:] if len(trace) > 10 else trace[8:])
         prev = ms
 
 
@@ -682,7 +684,7 @@ def main():
     wl = Workload(torch, qe, seed=0, names=names)
     for _ in range(args.warmup):
         wl.step()
-    settle_steps = settle(torch, wl)
+    settle_steps, settle_trace = settle(torch, wl)
     ms, wall = time_steps(torch, wl, args.steps)  # the headline: exactly --steps steps
     value = wl.step_bytes / (ms * 1e-3) / 1e9
     windows = [time_steps(torch, wl, args.steps)[0] for _ in range(SPREAD_WINDOWS)]
@@ -692,7 +694,8 @@ def main():
     if args.step_only:
         print(json.dumps({"metric": METRIC, "value": round(value, 1), "unit": "GB/s",
                           "ms_per_step": round(ms, 4), "steps": args.steps,
-                          "settle_steps": settle_steps, "spread": spread}), flush=True)
+                          "settle_steps": settle_steps, "settle_trace_ms": settle_trace,
+                          "spread": spread}), flush=True)
         return
     timings = kernel_timings(torch, qe, wl, args.steps)
 
@@ -732,7 +735,7 @@ def main():
                    "io": "bf16 in; bf16 + E4M3 / E2M1 out", "parallelism": "1 GPU"},
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "wall_ms_per_step": round(1e3 * wall, 4),
-        "settle_steps": settle_steps, "spread": spread,
+        "settle_steps": settle_steps, "settle_trace_ms": settle_trace, "spread": spread,
         "kernels": kernels,
         "extra_kernels": extra,
         "norm_rows": norm_rows,
@@ -742,7 +745,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": kernels[dom]["bytes"]},
     }
     if args.blocks:
-        out["block_sequence"] = block_sequence(torch, qe, args.blocks, reps=3)
+        out["block_sequence"] = block_sequence(torch, qe, args.blocks, reps=5)
     if not args.no_cpu:
         log("timing the CPU oracle on a row sample ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_div)
