@@ -709,6 +709,10 @@ def main():
                          "rotation_sets": t["sets"]}
         if nbytes < 32 << 20:  # short launches: also without the Python launch cost
             kernels[name]["graph_us_per_call"] = round(graph_us_per_call(torch, qe, name, nbytes), 3)
+    # The block sequence is timed right after the step's own launches, at the
+    # same steady state as the headline; the kernels beside the step, the
+    # short-row norms and the split path (about 20 s more of load) come after.
+    blocks = block_sequence(torch, qe, args.blocks, reps=5) if args.blocks else None
     extra = {} if args.only or args.no_extra else extra_timings(torch, qe, args.steps)
     norm_rows = {} if args.only or args.no_extra else norm_rows_timings(torch, qe, args.steps)
     split = {}
@@ -744,8 +748,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": kernels[dom]["bytes"]},
     }
-    if args.blocks:
-        out["block_sequence"] = block_sequence(torch, qe, args.blocks, reps=5)
+    if blocks:
+        out["block_sequence"] = blocks
     if not args.no_cpu:
         log("timing the CPU oracle on a row sample ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_div)
