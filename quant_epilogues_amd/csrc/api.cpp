@@ -141,6 +141,8 @@ int dit_norm_modulate_fp8_dual(void* img_y, uint8_t* img_q, const void* img_x,
     const char* fn = "dit_norm_modulate_fp8_dual";
     if (img_rows < 0 || txt_rows < 0)
         return fail(DIT_ERR_SHAPE, "%s: row counts must be >= 0", fn);
+    if (img_rows > kMaxRows || txt_rows > kMaxRows)  // keeps the sum below from overflowing
+        return fail(DIT_ERR_UNSUPPORTED, "%s: row counts too large", fn);
     if (int st = check_norm_shape(fn, img_rows + txt_rows, hidden)) return st;
     dit::NormModulateArgs img, txt;
     if (int st = dual_stream(fn, "img", img, img_y, img_q, img_x, img_scale, img_shift,
@@ -372,7 +374,8 @@ int dit_token_cat_quant(int32_t kind, uint8_t* out, uint8_t* out_scales, const v
     if (a_cols % 16 != 0 || b_cols % 16 != 0 || a_cols < 16)
         return fail(DIT_ERR_SHAPE, "%s: a_cols (%lld) and b_cols (%lld) must be multiples of 16, a_cols >= 16",
                     fn, (long long)a_cols, (long long)b_cols);
-    if (a_cols + b_cols > (int64_t(1) << 28) || rows > kMaxRows)
+    if (a_cols > (int64_t(1) << 28) || b_cols > (int64_t(1) << 28) ||
+        a_cols + b_cols > (int64_t(1) << 28) || rows > kMaxRows)
         return fail(DIT_ERR_UNSUPPORTED, "%s: shape too large", fn);
     if (kind == DIT_QUANT_FP4_E2M1_128X4 && (a_cols + b_cols) % 64 != 0)
         return fail(DIT_ERR_UNSUPPORTED, "%s: the 128x4 scale layout needs a_cols + b_cols %% 64 == 0",

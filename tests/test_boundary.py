@@ -114,6 +114,7 @@ def test_norm_modulate_dual_refusals(native):
     assert _dual(L, irows=0, trows=0, ix=None, tx=None) == native.DIT_OK
     assert _dual(L, irows=0, ix=None, iy=None, iq=None, tx=FAKE + 8) == native.DIT_ERR_ALIGN
     assert _dual(L, irows=1 << 30) == native.DIT_ERR_UNSUPPORTED
+    assert _dual(L, irows=1 << 62, trows=1 << 62) == native.DIT_ERR_UNSUPPORTED  # no overflow
 
 
 def test_scale_residual_refusals(native):
@@ -190,6 +191,8 @@ def test_token_cat_refusals(native):
     assert f(fp8, FAKE, None, FAKE, 6144, None, 18432, 4, FAKE, None) == native.DIT_ERR_NULL
     assert f(fp8, FAKE + 8, None, FAKE, 6144, FAKE2, 18432, 4, FAKE, None) == native.DIT_ERR_ALIGN
     assert f(fp4, FAKE, FAKE, FAKE, 6144, None, 0, 0, FAKE, None) == native.DIT_OK
+    huge = (1 << 62) + 16  # a multiple of 16 whose sum with itself overflows int64
+    assert f(fp8, FAKE, None, FAKE, huge, FAKE2, huge, 4, FAKE, None) == native.DIT_ERR_UNSUPPORTED
 
 
 def test_python_binding_has_no_cpu_path(native):
