@@ -208,6 +208,49 @@ def test_norm_modulate_fp8_dual_equals_two_calls(qe):
                 assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+DUAL_SELECT_CASES = [
+    # (img_rows, txt_rows, hidden, img outputs, txt outputs, seed); the geometry
+    # at 6144 follows whether the text rows (the first set) write y
+    (1000, 200, 3072, "yq", "q", 70),
+    (1000, 200, 3072, "q", "y", 71),
+    (2000, 100, 6144, "y", "q", 72),
+    (2000, 100, 6144, "q", "yq", 73),
+]
+
+
+@pytest.mark.parametrize("img_rows,txt_rows,hidden,img_out,txt_out,seed", DUAL_SELECT_CASES)
+def test_norm_modulate_fp8_dual_output_selection(qe, oracle_mod, e4m3_table, img_rows, txt_rows,
+                                                 hidden, img_out, txt_out, seed):
+    """Each row set of the one-launch norm writes only the outputs it asks for,
+    and those equal the oracle's."""
+    _print_case("norm_modulate_fp8_dual selection", img_rows, txt_rows, hidden, img_out, txt_out,
+                seed)
+    img = synth.norm_modulate_inputs(img_rows, hidden, seed=seed, input_scale=0.0625)
+    txt = synth.norm_modulate_inputs(txt_rows, hidden, seed=seed + 1000, input_scale=0.02,
+                                     eps=1e-5)
+    out = {}
+    for name, rows, sel in (("img", img_rows, img_out), ("txt", txt_rows, txt_out)):
+        out[name] = (Guarded((rows, hidden), torch.bfloat16) if "y" in sel else None,
+                     Guarded((rows, hidden), torch.uint8) if "q" in sel else None)
+    ptr = lambda g: None if g is None else g.t
+    (iy, iq), (ty, tq) = out["img"], out["txt"]
+    qe.dit_norm_modulate_fp8_dual(
+        ptr(iy), ptr(iq), dev(img.x), dev(img.scale), dev(img.shift), dscalar(img.input_scale),
+        img_rows, img.eps, ptr(ty), ptr(tq), dev(txt.x), dev(txt.scale), dev(txt.shift),
+        dscalar(txt.input_scale), txt_rows, txt.eps, hidden)
+    torch.cuda.synchronize()
+    for name, inp in (("img", img), ("txt", txt)):
+        y, q = out[name]
+        ry, rq, pre = oracle_mod.norm_modulate_fp8(bits(inp.x), bits(inp.scale), bits(inp.shift),
+                                                   inp.input_scale, inp.eps)
+        if y is not None:
+            y.check(name + " y")
+            check_bf16(name + " y", y.bits(), ry)
+        if q is not None:
+            q.check(name + " q")
+            check_fp8(name + " q", q.bits(), rq, pre, e4m3_table)
+
+
 SR_CASES = [
     (4096, 3072, 0.02, True, 0),
     (4096, 3072, 0.0625, True, 1),
