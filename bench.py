@@ -465,20 +465,22 @@ def block_sequence(torch, qe, blocks, reps):
     FP8 of the image and text rows (one launch), the QKV epilogue and
     bias_mul_add, each block on its own random buffers."""
     wls = [Workload(torch, qe, seed=100 + i, names=BLOCK_LAUNCHES) for i in range(blocks)]
-    for wl in wls:
-        wl.step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
+    for _ in range(2):  # untimed: the GPU idled while the buffers were set up
         for wl in wls:
             wl.step()
-    end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / reps
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    events[0].record()
+    for i in range(reps):
+        for wl in wls:
+            wl.step()
+        events[i + 1].record()
+    torch.cuda.synchronize()
+    passes = [events[i].elapsed_time(events[i + 1]) for i in range(reps)]
+    ms = statistics.median(passes)
     nbytes = sum(wl.step_bytes for wl in wls)
     return {"blocks": blocks, "launches": len(BLOCK_LAUNCHES) * blocks, "bytes": nbytes,
-            "ms_per_pass": round(ms, 4),
+            "ms_per_pass": round(ms, 4), "ms_passes": [round(min(passes), 4), round(max(passes), 4)],
             "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
