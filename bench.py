@@ -289,7 +289,7 @@ def settle(torch, wl):
         prev = ms
 
 
-KERNEL_PASSES = 3
+KERNEL_PASSES = 5
 
 
 def kernel_timings(torch, qe, wl, steps):
