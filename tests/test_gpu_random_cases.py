@@ -222,3 +222,37 @@ def test_random_qkv(qe, oracle_mod, i):
     check_bf16("joint_q", gq, rq)
     check_bf16("joint_k", gk, rk)
     check_exact("joint_v", gv, rv)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_norm_dual(qe, oracle_mod, e4m3_table, i):
+    rng = np.random.default_rng(10000 + i)
+    hidden = 8 * int(rng.integers(1, 1025))
+    cap = max(2, min(3000, 3_000_000 // hidden))
+    img_rows, txt_rows = int(rng.integers(0, cap)), int(rng.integers(0, cap // 4 + 1))
+    outs = {"img": str(rng.choice(["yq", "y", "q"])), "txt": str(rng.choice(["yq", "y", "q"]))}
+    _print_case("random norm dual", img_rows, txt_rows, hidden, outs, i)
+    g = torch.Generator().manual_seed(11000 + i)
+    sets = {}
+    for name, rows in (("img", img_rows), ("txt", txt_rows)):
+        x = _rows_bf16(g, rows, hidden)
+        scale, shift = _vec(g, hidden, 0.0, 0.3), _vec(g, hidden, 0.0, 0.3)
+        s = _log_uniform(rng, 1e-3, 1e2)
+        eps = float(rng.choice([1e-6, 1e-5, 1e-3]))
+        y = Guarded((rows, hidden), torch.bfloat16) if "y" in outs[name] else None
+        q = Guarded((rows, hidden), torch.uint8) if "q" in outs[name] else None
+        sets[name] = (x, scale, shift, s, eps, y, q)
+    ptr = lambda o: None if o is None else o.t  # noqa: E731
+    (ix, isc, ish, is_, ie, iy, iq), (tx, tsc, tsh, ts, te, ty, tq) = sets["img"], sets["txt"]
+    qe.dit_norm_modulate_fp8_dual(ptr(iy), ptr(iq), dev(ix), dev(isc), dev(ish), dscalar(is_),
+                                  img_rows, ie, ptr(ty), ptr(tq), dev(tx), dev(tsc), dev(tsh),
+                                  dscalar(ts), txt_rows, te, hidden)
+    torch.cuda.synchronize()
+    for name, (x, scale, shift, s, eps, y, q) in sets.items():
+        ry, rq, pre = oracle_mod.norm_modulate_fp8(bits(x), bits(scale), bits(shift), s, eps)
+        if y is not None:
+            y.check(name + " y")
+            check_bf16(name + " y", y.bits(), ry)
+        if q is not None:
+            q.check(name + " q")
+            check_fp8(name + " q", q.bits(), rq, pre, e4m3_table)
